@@ -1,0 +1,13 @@
+"""Block-scaled FP8 GEMM for AMD Instinct MI355X (gfx950).
+
+The compute path is the C-ABI library ``libfp8gemm.so`` (hand-written HIP
+kernels, built by :mod:`fp8_block_scaled_04_amd.build`); :mod:`.binding`
+exposes its entry points under the same names.  :mod:`.synth` generates the
+seeded synthetic inputs used by the tests and the benchmark.
+"""
+from .binding import (  # noqa: F401
+    FP8G_BF16, FP8G_EINVAL, FP8G_ELAUNCH, FP8G_EUNSUPPORTED, FP8G_F32, FP8G_OK,
+    Fp8GemmError, fp8_cast_per_block, fp8_cast_per_token_group, fp8_gemm_nt,
+    fp8_gemm_workspace_bytes, fp8_get_num_cus, fp8_grouped_gemm_contiguous,
+    fp8_grouped_gemm_masked, fp8_set_num_cus, fp8_status_string,
+)

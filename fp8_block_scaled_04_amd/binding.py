@@ -1,0 +1,208 @@
+"""ctypes binding of libfp8gemm.so, with the C ABI's names.
+
+Argument marshalling only: tensors are PyTorch device tensors (PyTorch is
+used for device memory and streams); every step of the computation runs in
+the library's HIP kernels.  There is no fallback path: if the library is
+missing, every call raises.
+
+Layouts (see include/fp8gemm.h): FP8 tensors are uint8 (or
+torch.float8_e4m3fn) codes; LHS scales are MN-major ``[KG][ld]`` float32;
+RHS scales ``[NB][KG]`` (``[G][NB][KG]`` grouped) float32; outputs bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+from . import build as _build
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = _build.LIB
+HEADER = os.path.join(os.path.dirname(HERE), "include", "fp8gemm.h")
+
+FP8G_OK, FP8G_EINVAL, FP8G_EUNSUPPORTED, FP8G_ELAUNCH = 0, -1, -2, -3
+FP8G_F32, FP8G_BF16 = 0, 1
+
+_lib = None
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+_SIGNATURES = {
+    "fp8_gemm_nt": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "fp8_grouped_gemm_contiguous": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "fp8_grouped_gemm_masked": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "fp8_cast_per_token_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
+    "fp8_cast_per_block": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
+    "fp8_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
+    "fp8_set_num_cus": ([_i32], _i32),
+    "fp8_get_num_cus": ([], _i32),
+    "fp8_status_string": ([_i32], ctypes.c_char_p),
+}
+
+
+class Fp8GemmError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+def lib():
+    """Load libfp8gemm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with fp8_block_scaled_04_amd.build.build()")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def header_functions():
+    """Names of the functions declared in include/fp8gemm.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8_\w+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().fp8_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != FP8G_OK:
+        raise Fp8GemmError(fn, status)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _codes(t, name):
+    if t.dtype == torch.float8_e4m3fn:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+    return _dev(t, name)
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _f32(t, name):
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _bf16(t, name):
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+    return _dev(t, name)
+
+
+def _i32t(t, name):
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    return _dev(t, name)
+
+
+# ---- entry points ------------------------------------------------------------
+def fp8_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace=None, stream=None):
+    """out[m][n] = block-scaled FP8 NT GEMM of lhs [m][k] and rhs [n][k].
+    lhs_scales is MN-major [KG][ld >= m]; rhs_scales [NB][KG]."""
+    lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out = _bf16(out, "out")
+    m, k = lhs.shape
+    n = rhs.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fp8_gemm_nt(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales), _p(out),
+                           m, n, k, _p(workspace), ws_bytes, _stream(stream))
+    _check("fp8_gemm_nt", st)
+    return out
+
+
+def fp8_grouped_gemm_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices, stream=None):
+    """Contiguous-layout grouped GEMM: lhs [M][k], rhs [G][n][k], m_indices [M]."""
+    lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out, m_indices = _bf16(out, "out"), _i32t(m_indices, "m_indices")
+    M, k = lhs.shape
+    G, n, _ = rhs.shape
+    st = lib().fp8_grouped_gemm_contiguous(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales),
+                                           _p(out), _p(m_indices), M, n, k, G, None, 0, _stream(stream))
+    _check("fp8_grouped_gemm_contiguous", st)
+    return out
+
+
+def fp8_grouped_gemm_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m, stream=None):
+    """Masked-layout grouped GEMM: lhs [G][max_m][k], lhs_scales [G][KG][ld],
+    rhs [G][n][k], masked_m [G] (device int32)."""
+    lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out, masked_m = _bf16(out, "out"), _i32t(masked_m, "masked_m")
+    G, max_m, k = lhs.shape
+    n = rhs.shape[1]
+    st = lib().fp8_grouped_gemm_masked(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales),
+                                       _p(out), _p(masked_m), G, max_m, n, k, None, 0, _stream(stream))
+    _check("fp8_grouped_gemm_masked", st)
+    return out
+
+
+def fp8_cast_per_token_group(x, q, scales, stream=None):
+    """x [m][k] float32 or bfloat16 -> q [m][k] codes, scales [KG][ld >= m]."""
+    x = _dev(x, "x")
+    if x.dtype == torch.float32:
+        dt = FP8G_F32
+    elif x.dtype == torch.bfloat16:
+        dt = FP8G_BF16
+    else:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    q, scales = _codes(q, "q"), _f32(scales, "scales")
+    m, k = x.shape
+    st = lib().fp8_cast_per_token_group(_p(x), dt, m, k, _p(q), _p(scales), scales.shape[-1], _stream(stream))
+    _check("fp8_cast_per_token_group", st)
+    return q, scales
+
+
+def fp8_cast_per_block(w, q, scales, stream=None):
+    """w [n][k] float32 -> q [n][k] codes, scales [NB][KG] (128 x 128 blocks)."""
+    w = _f32(w, "w")
+    q, scales = _codes(q, "q"), _f32(scales, "scales")
+    n, k = w.shape
+    st = lib().fp8_cast_per_block(_p(w), n, k, _p(q), _p(scales), _stream(stream))
+    _check("fp8_cast_per_block", st)
+    return q, scales
+
+
+def fp8_gemm_workspace_bytes(m, n, k, num_groups=1) -> int:
+    return int(lib().fp8_gemm_workspace_bytes(int(m), int(n), int(k), int(num_groups)))
+
+
+def fp8_set_num_cus(num_cus: int) -> int:
+    return int(lib().fp8_set_num_cus(int(num_cus)))
+
+
+def fp8_get_num_cus() -> int:
+    return int(lib().fp8_get_num_cus())
+
+
+def fp8_status_string(status: int) -> str:
+    return status_string(status)

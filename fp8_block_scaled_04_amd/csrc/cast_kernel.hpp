@@ -1,0 +1,117 @@
+// FP8 E4M3 casts for gfx950: per-token-group (1 x 128, activations) and per
+// 128 x 128 block (weights).
+//
+// What is computed (kwkr.cn DeepGEMM usage article, section 3.1 and the code
+// in section 4.2; "DeepSeek open-source week, day 3: DeepGEMM", "Basic usage"
+// scale shapes): amax = max |x| over the group or block, scale =
+// fl32(amax / 448) (1.0 for an all-zero group, a reading the pages leave
+// open), q = E4M3(fl32(x / scale)).  Division is IEEE fp32 correctly rounded
+// (no reciprocal shortcut), so codes and scales are reproducible bit for bit.
+// The hardware conversion rounds to nearest-even; values are first clamped to
+// +-448, so the conversion saturates instead of producing NaN above 464.
+//
+// Both kernels are HBM-bound (5 B moved per element, a handful of ALU ops):
+// 16-byte loads, one wave-local amax reduction, packed stores.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace fp8g {
+
+__device__ __forceinline__ float group_scale(float amax) {
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+}
+
+// Four fp32 -> four E4M3 codes in one dword (element 0 in the low byte).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return uint32_t(w);
+}
+
+__device__ __forceinline__ void load8(const float* x, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(x);
+  const float4 b = *reinterpret_cast<const float4*>(x + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+__device__ __forceinline__ void load8(const uint16_t* x, float v[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(x);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+
+// Per-token-group cast.  Grid (ceil(m / 16), KG), 256 threads: 16 lanes per
+// (row, group), 8 consecutive elements per lane.  Scales are written
+// MN-major, scales[g * ld + row], 16 consecutive rows per workgroup.
+template <typename T>
+__global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x, int m, int k,
+                                                         uint8_t* __restrict__ q,
+                                                         float* __restrict__ scales, int64_t ld) {
+  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int g = blockIdx.y;
+  const int col = g * 128 + (threadIdx.x & 15) * 8;
+  const bool live = row < m && col < k;
+  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (live) load8(x + int64_t(row) * k + col, v);
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+  const float s = group_scale(amax);
+  if (live) {
+    uint2 w;
+    w.x = e4m3x4(__fdiv_rn(v[0], s), __fdiv_rn(v[1], s), __fdiv_rn(v[2], s), __fdiv_rn(v[3], s));
+    w.y = e4m3x4(__fdiv_rn(v[4], s), __fdiv_rn(v[5], s), __fdiv_rn(v[6], s), __fdiv_rn(v[7], s));
+    *reinterpret_cast<uint2*>(q + int64_t(row) * k + col) = w;
+    if ((threadIdx.x & 15) == 0) scales[int64_t(g) * ld + row] = s;
+  }
+}
+
+// 128 x 128 block cast.  Grid (NB, KG), 256 threads.  Each load instruction
+// of a wave covers two 512-byte row segments (32 lanes x 16 B); a thread
+// holds 16 rows x 4 columns.  k must be a multiple of 4.
+__global__ void __launch_bounds__(256) cast_128x128_kernel(const float* __restrict__ w, int n, int k,
+                                                          uint8_t* __restrict__ q,
+                                                          float* __restrict__ scales, int kg) {
+  __shared__ float wave_max[4];
+  const int nb = blockIdx.x, g = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = g * 128 + (lane & 31) * 4;
+  const bool col_ok = col < k;
+  float4 v[16];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = nb * 128 + wave * 32 + 2 * i + (lane >> 5);
+    v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < n && col_ok) v[i] = *reinterpret_cast<const float4*>(w + int64_t(row) * k + col);
+    amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  if (lane == 0) wave_max[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
+  const float s = group_scale(amax);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = nb * 128 + wave * 32 + 2 * i + (lane >> 5);
+    if (row < n && col_ok)
+      *reinterpret_cast<uint32_t*>(q + int64_t(row) * k + col) =
+          e4m3x4(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s), __fdiv_rn(v[i].z, s), __fdiv_rn(v[i].w, s));
+  }
+  if (threadIdx.x == 0) scales[int64_t(nb) * kg + g] = s;
+}
+
+}  // namespace fp8g

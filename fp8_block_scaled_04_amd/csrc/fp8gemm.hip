@@ -1,0 +1,291 @@
+// Host side of the C-ABI library libfp8gemm.so (declared in fp8gemm.h):
+// argument validation, the shape -> kernel configuration choice, grid sizing
+// for the CU budget, and the launches.  Nothing here synchronises or reads
+// device memory; every failure the host can detect is returned before any
+// launch.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstdio>
+
+#include "fp8gemm.h"
+#include "cast_kernel.hpp"
+#include "gemm_kernel.hpp"
+
+namespace {
+
+using fp8g::GemmParams;
+using fp8g::gemm_kernel;
+using fp8g::kContiguous;
+using fp8g::kDense;
+using fp8g::kMasked;
+
+std::atomic<int> g_cu_limit{0};
+
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
+}
+
+int effective_cus() {
+  const int d = device_cus();
+  const int lim = g_cu_limit.load();
+  return (lim > 0 && lim < d) ? lim : d;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* v = std::getenv("FP8G_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+int launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    if (log_enabled()) std::fprintf(stderr, "[fp8gemm] %s launch failed: %s\n", what, hipGetErrorString(e));
+    return FP8G_ELAUNCH;
+  }
+  return FP8G_OK;
+}
+
+// Common GEMM shape limits of this version.
+int check_gemm_shape(int n, int k) {
+  if (n < 0 || k < 0) return FP8G_EINVAL;
+  if (k == 0 || k % 128 != 0 || k / 128 > fp8g::kMaxGroups) return FP8G_EUNSUPPORTED;
+  if (n % 8 != 0) return FP8G_EUNSUPPORTED;
+  return FP8G_OK;
+}
+
+int check_ld(int64_t ld, int64_t rows) {
+  if (ld < rows || ld % 4 != 0 || ld < 4) return FP8G_EUNSUPPORTED;
+  return FP8G_OK;
+}
+
+// ---- dense configuration ---------------------------------------------------
+// Kernel shapes (BM tokens x BN outputs per workgroup, wave grid, LDS stages):
+//   kDenseM64   64 x 128, waves 1x4, 4 stages  (m <= 64)
+//   kDenseM128 128 x 128, waves 2x2, 3 stages  (m <= 128)
+//   kDenseBig  256 x 128, waves 2x2, 3 stages  (m > 128)
+// A wave's accumulator tile is at most 128 x 64 (128 VGPRs): the promotion
+// FMAs need their accumulators in the 256 architectural VGPRs.
+// When the tile count would leave CUs idle, K is split across workgroups and
+// the partials are summed in a fixed order.
+enum DenseKind { kDenseM64 = 0, kDenseM128 = 1, kDenseBig = 2 };
+
+struct DenseConfig {
+  int kind, bm, bn, tiles_m, tiles_n, splits, gps;
+};
+
+DenseConfig dense_config(int m, int n, int k, bool allow_split) {
+  DenseConfig c{};
+  if (m <= 64) { c.kind = kDenseM64; c.bm = 64; c.bn = 128; }
+  else if (m <= 128) { c.kind = kDenseM128; c.bm = 128; c.bn = 128; }
+  else { c.kind = kDenseBig; c.bm = 256; c.bn = 128; }
+  c.tiles_m = int(cdiv(m, c.bm));
+  c.tiles_n = int(cdiv(n, c.bn));
+  const int kg = k / 128;
+  c.splits = 1;
+  c.gps = kg;
+  const int64_t tiles = int64_t(c.tiles_m) * c.tiles_n;
+  const int cus = effective_cus();
+  if (allow_split && tiles < cus) {
+    int s = int(std::min<int64_t>(kg, cdiv(cus, tiles)));
+    const char* force = std::getenv("FP8G_SPLITS");
+    if (force) s = std::max(1, std::min(kg, std::atoi(force)));
+    c.gps = int(cdiv(kg, s));
+    c.splits = int(cdiv(kg, c.gps));
+  }
+  return c;
+}
+
+size_t dense_workspace(const DenseConfig& c, int m, int n) {
+  return c.splits > 1 ? size_t(c.splits) * size_t(m) * size_t(n) * sizeof(float) : 0;
+}
+
+template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT>
+void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT>), dim3(unsigned(grid)), dim3(256), 0, s, p);
+}
+
+template <bool SPLIT>
+void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+  switch (kind) {
+    case kDenseM64: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
+    case kDenseM128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
+    default: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp8_status_string(int status) {
+  switch (status) {
+    case FP8G_OK: return "ok";
+    case FP8G_EINVAL: return "invalid argument";
+    case FP8G_EUNSUPPORTED: return "unsupported shape or layout";
+    case FP8G_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int fp8_set_num_cus(int num_cus) {
+  const int prev = g_cu_limit.load();
+  g_cu_limit.store(num_cus < 0 ? 0 : num_cus);
+  return prev;
+}
+
+int fp8_get_num_cus(void) { return effective_cus(); }
+
+size_t fp8_gemm_workspace_bytes(int m, int n, int k, int num_groups) {
+  (void)num_groups;
+  if (m <= 0 || n <= 0 || k <= 0 || k % 128 != 0) return 0;
+  const DenseConfig c = dense_config(m, n, k, true);
+  return dense_workspace(c, m, n);
+}
+
+int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                const uint8_t* rhs, const float* rhs_scales, uint16_t* out, int m, int n, int k,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0) return FP8G_EINVAL;
+  if (int st = check_gemm_shape(n, k)) return st;
+  if (m == 0 || n == 0) return FP8G_OK;
+  if (!lhs || !lhs_scales || !rhs || !rhs_scales || !out) return FP8G_EINVAL;
+  if (!aligned16(lhs) || !aligned16(lhs_scales) || !aligned16(rhs) || !aligned16(rhs_scales) ||
+      !aligned16(out) || (workspace && !aligned16(workspace)))
+    return FP8G_EINVAL;
+  if (int st = check_ld(lhs_scales_ld, m)) return st;
+
+  DenseConfig c = dense_config(m, n, k, true);
+  if (c.splits > 1 && (!workspace || workspace_bytes < dense_workspace(c, m, n))) c = dense_config(m, n, k, false);
+
+  GemmParams p{};
+  p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
+  p.partial = static_cast<float*>(workspace);
+  p.sa_ld = lhs_scales_ld;
+  p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
+  p.tiles_m = c.tiles_m; p.tiles_n = c.tiles_n; p.splits = c.splits; p.groups_per_split = c.gps;
+  const int64_t grid = int64_t(c.tiles_m) * c.tiles_n * c.splits;
+  auto s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
+                 c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
+  if (c.splits > 1) {
+    launch_dense<true>(c.kind, p, grid, s);
+    if (int st = launched("gemm")) return st;
+    const int64_t mn = int64_t(m) * n;
+    hipLaunchKernelGGL(fp8g::splitk_reduce_kernel, dim3(unsigned(cdiv(mn / 4, 256))), dim3(256), 0, s,
+                       static_cast<const float*>(workspace), out, mn, c.splits);
+    return launched("split-K reduce");
+  }
+  launch_dense<false>(c.kind, p, grid, s);
+  return launched("gemm");
+}
+
+int fp8_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                                const uint8_t* rhs, const float* rhs_scales, uint16_t* out,
+                                const int32_t* m_indices, int m_total, int n, int k, int num_groups,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (m_total < 0 || num_groups < 0) return FP8G_EINVAL;
+  if (int st = check_gemm_shape(n, k)) return st;
+  if (m_total % 128 != 0) return FP8G_EUNSUPPORTED;
+  if (m_total == 0 || n == 0 || num_groups == 0) return FP8G_OK;
+  if (!lhs || !lhs_scales || !rhs || !rhs_scales || !out || !m_indices) return FP8G_EINVAL;
+  if (!aligned16(lhs) || !aligned16(lhs_scales) || !aligned16(rhs) || !aligned16(rhs_scales) ||
+      !aligned16(out) || !aligned16(m_indices))
+    return FP8G_EINVAL;
+  if (int st = check_ld(lhs_scales_ld, m_total)) return st;
+
+  GemmParams p{};
+  p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
+  p.m_indices = m_indices;
+  p.sa_ld = lhs_scales_ld;
+  p.m = m_total; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
+  p.tiles_m = m_total / 128; p.tiles_n = int(cdiv(n, 256)); p.splits = 1; p.groups_per_split = p.kg;
+  const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
+  if (log_enabled())
+    std::fprintf(stderr, "[fp8gemm] contiguous M=%d n=%d k=%d G=%d grid=%lld\n", m_total, n, k, num_groups,
+                 (long long)grid);
+  launch_gemm<128, 256, 1, 4, 3, kContiguous, false>(p, grid, static_cast<hipStream_t>(stream));
+  return launched("contiguous gemm");
+}
+
+int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                            const uint8_t* rhs, const float* rhs_scales, uint16_t* out,
+                            const int32_t* masked_m, int num_groups, int max_m, int n, int k,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  (void)workspace; (void)workspace_bytes;
+  if (num_groups < 0 || max_m < 0) return FP8G_EINVAL;
+  if (int st = check_gemm_shape(n, k)) return st;
+  if (num_groups == 0 || max_m == 0 || n == 0) return FP8G_OK;
+  if (!lhs || !lhs_scales || !rhs || !rhs_scales || !out || !masked_m) return FP8G_EINVAL;
+  if (!aligned16(lhs) || !aligned16(lhs_scales) || !aligned16(rhs) || !aligned16(rhs_scales) ||
+      !aligned16(out) || !aligned16(masked_m))
+    return FP8G_EINVAL;
+  if (int st = check_ld(lhs_scales_ld, max_m)) return st;
+
+  GemmParams p{};
+  p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
+  p.masked_m = masked_m;
+  p.sa_ld = lhs_scales_ld;
+  p.m = max_m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
+  p.tiles_m = int(cdiv(max_m, 256)); p.tiles_n = int(cdiv(n, 128)); p.splits = 1; p.groups_per_split = p.kg;
+  const int64_t grid = int64_t(p.tiles_m) * p.tiles_n * num_groups;
+  if (log_enabled())
+    std::fprintf(stderr, "[fp8gemm] masked G=%d max_m=%d n=%d k=%d grid=%lld\n", num_groups, max_m, n, k,
+                 (long long)grid);
+  launch_gemm<256, 128, 2, 2, 3, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
+  return launched("masked gemm");
+}
+
+int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k, uint8_t* q, float* scales,
+                             int64_t scales_ld, void* stream) {
+  if (m < 0 || k < 0) return FP8G_EINVAL;
+  if (x_dtype != FP8G_F32 && x_dtype != FP8G_BF16) return FP8G_EINVAL;
+  if (k % 8 != 0) return FP8G_EUNSUPPORTED;
+  if (m == 0 || k == 0) return FP8G_OK;
+  if (!x || !q || !scales) return FP8G_EINVAL;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return FP8G_EINVAL;
+  if (scales_ld < m) return FP8G_EUNSUPPORTED;
+  const int64_t kg = cdiv(k, 128);
+  if (kg > 65535) return FP8G_EUNSUPPORTED;
+  const dim3 grid(unsigned(cdiv(m, 16)), unsigned(kg));
+  auto s = static_cast<hipStream_t>(stream);
+  if (x_dtype == FP8G_F32)
+    hipLaunchKernelGGL(fp8g::cast_1x128_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(x), m, k,
+                       q, scales, scales_ld);
+  else
+    hipLaunchKernelGGL(fp8g::cast_1x128_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
+                       m, k, q, scales, scales_ld);
+  return launched("per-token-group cast");
+}
+
+int fp8_cast_per_block(const float* w, int n, int k, uint8_t* q, float* scales, void* stream) {
+  if (n < 0 || k < 0) return FP8G_EINVAL;
+  if (k % 4 != 0) return FP8G_EUNSUPPORTED;
+  if (n == 0 || k == 0) return FP8G_OK;
+  if (!w || !q || !scales) return FP8G_EINVAL;
+  if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FP8G_EINVAL;
+  const int64_t kg = cdiv(k, 128), nb = cdiv(n, 128);
+  if (kg > 65535 || nb > 0x7fffffff) return FP8G_EUNSUPPORTED;
+  hipLaunchKernelGGL(fp8g::cast_128x128_kernel, dim3(unsigned(nb), unsigned(kg)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), w, n, k, q, scales, int(kg));
+  return launched("block cast");
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+/* fp8gemm.h -- block-scaled FP8 GEMM library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes is defined on "DeepSeek open-source week, day 3:
+ * DeepGEMM" (explinks.com): an FP8 E4M3 GEMM in NT layout (LHS m x k not
+ * transposed, RHS n x k "transposed", both K-contiguous) with fine-grained
+ * scaling -- one FP32 scale per row and 128-wide K group on the LHS, one FP32
+ * scale per 128 x 128 block on the RHS -- and a BF16 output ("Basic usage"
+ * example); partial products are promoted into an FP32 accumulator once per
+ * 128-wide K group, final += (scale_a * scale_b) * partial ("Core features",
+ * two-level accumulation; "Source walk-through" part 3).  The same core runs
+ * as a dense GEMM, as a contiguous-layout grouped GEMM (MoE prefill: experts'
+ * rows concatenated along M) and as a masked-layout grouped GEMM (MoE decode:
+ * a fixed slot per group plus a device tensor of valid row counts, so the
+ * host never learns them) -- the page's three GEMM kinds.  Per-token-group
+ * activation quantisation (scale = amax / 448, q = fp8(x / scale)) follows
+ * the kwkr.cn DeepGEMM usage article, section 3.1 and its section 4.2 code.
+ *
+ * Conventions for every entry point
+ *   - Tensor pointers are DEVICE pointers to dense row-major storage.  FP8
+ *     tensors hold OCP E4M3FN codes (uint8); BF16 tensors hold bit patterns
+ *     (uint16); scales are FP32.  Every pointer must be 16-byte aligned.
+ *   - KG = ceil(k / 128) and NB = ceil(n / 128).
+ *   - LHS scales are stored MN-major: element (row r, K group g) lives at
+ *     lhs_scales[g * lhs_scales_ld + r], with lhs_scales_ld >= rows and
+ *     lhs_scales_ld % 4 == 0.  RHS scales are row-major [NB][KG].
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
+ *     asynchronous on that stream, never synchronises and never reads device
+ *     data on the host, so calls may be captured into a HIP graph.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     retains caller memory.
+ *   - Errors that the host can check are reported before anything is
+ *     launched: FP8G_EINVAL for null pointers, negative sizes or misaligned
+ *     pointers; FP8G_EUNSUPPORTED for shapes outside this version's limits
+ *     (k % 128 != 0, n % 8 != 0, contiguous m_total % 128 != 0, a bad
+ *     scales ld); FP8G_ELAUNCH if the launch itself fails.  No C++ exception
+ *     crosses this interface.
+ *   - Zero-sized problems (m = 0, n = 0, num_groups = 0) succeed and launch
+ *     nothing.
+ */
+#ifndef FP8GEMM_H
+#define FP8GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  FP8G_OK = 0,
+  FP8G_EINVAL = -1,
+  FP8G_EUNSUPPORTED = -2,
+  FP8G_ELAUNCH = -3
+};
+
+/* Element type of the cast helper's input. */
+enum { FP8G_F32 = 0, FP8G_BF16 = 1 };
+
+/* Dense NT GEMM: out[m][n] = bf16( sum_k dec(lhs[i][t]) * sa(i, t/128)
+ *                                        * dec(rhs[j][t]) * sb(j/128, t/128) ),
+ * evaluated with one FP32 promotion per 128-wide K group.
+ *   lhs        [m][k] E4M3 codes;   lhs_scales [KG][lhs_scales_ld] FP32
+ *   rhs        [n][k] E4M3 codes;   rhs_scales [NB][KG] FP32
+ *   out        [m][n] BF16 (written in full)
+ *   workspace  optional device scratch for split-K partial sums; pass the
+ *              size reported by fp8_gemm_workspace_bytes() to allow split-K.
+ *              A smaller (or NULL) workspace selects a configuration without
+ *              split-K; it is never an error.  The result does not depend on
+ *              whether split-K is used up to FP32 rounding order, and a given
+ *              configuration always produces bit-identical output. */
+int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                const uint8_t* rhs, const float* rhs_scales,
+                uint16_t* out, int m, int n, int k,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Contiguous-layout grouped GEMM (MoE prefill / training forward).
+ *   lhs        [m_total][k];  lhs_scales [KG][lhs_scales_ld >= m_total]
+ *   rhs        [num_groups][n][k];  rhs_scales [num_groups][NB][KG]
+ *   m_indices  [m_total] int32 on the device: the group of each row.  Rows
+ *              are consumed in aligned blocks of 128; every row of a block
+ *              must carry the same index (each expert's row count is a
+ *              multiple of 128).  A negative index marks a block whose
+ *              output rows are left untouched.  An index >= num_groups is
+ *              undefined behaviour.
+ *   out        [m_total][n] BF16
+ *   m_total % 128 must be 0.  The workspace is not used (may be NULL). */
+int fp8_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                                const uint8_t* rhs, const float* rhs_scales,
+                                uint16_t* out, const int32_t* m_indices,
+                                int m_total, int n, int k, int num_groups,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Masked-layout grouped GEMM (MoE decode).
+ *   lhs        [num_groups][max_m][k];
+ *   lhs_scales [num_groups][KG][lhs_scales_ld >= max_m]
+ *   rhs        [num_groups][n][k];  rhs_scales [num_groups][NB][KG]
+ *   masked_m   [num_groups] int32 on the device: valid rows per group,
+ *              clamped to [0, max_m].  Only rows r < masked_m[g] of group g
+ *              are computed and written; every other row of `out` is left
+ *              untouched, and whatever the LHS rows or scales past the count
+ *              hold (NaN codes included) cannot reach a written element.
+ *   out        [num_groups][max_m][n] BF16
+ *   The workspace is not used (may be NULL). */
+int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                            const uint8_t* rhs, const float* rhs_scales,
+                            uint16_t* out, const int32_t* masked_m,
+                            int num_groups, int max_m, int n, int k,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-token-group cast (kwkr.cn usage article, section 3.1 and 4.2 code):
+ * for each row and each 128-wide K group, amax = max |x|, scale =
+ * fl32(amax / 448) (1.0 when amax == 0), q = E4M3(fl32(x / scale)) rounded to
+ * nearest-even (saturating at +-448), with IEEE correctly rounded fp32
+ * division.  Inputs must be finite.
+ *   x       [m][k] FP32 (x_dtype FP8G_F32) or BF16 bits (FP8G_BF16)
+ *   q       [m][k] E4M3 codes
+ *   scales  [KG][scales_ld >= m] FP32 (the MN-major layout the GEMMs read) */
+int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
+                             uint8_t* q, float* scales, int64_t scales_ld, void* stream);
+
+/* 128 x 128 block cast for weights (the RHS scale granularity of the
+ * "Basic usage" example): one scale per block, computed as above over the
+ * block's real elements (edge blocks may be partial).
+ *   w       [n][k] FP32;  q [n][k] E4M3 codes;  scales [NB][KG] FP32 */
+int fp8_cast_per_block(const float* w, int n, int k,
+                       uint8_t* q, float* scales, void* stream);
+
+/* Workspace bytes that let fp8_gemm_nt choose split-K for this shape
+ * (0 = never needed).  An upper bound; depends on the CU limit in force. */
+size_t fp8_gemm_workspace_bytes(int m, int n, int k, int num_groups);
+
+/* Limit the number of compute units the GEMM schedulers size their grids
+ * for (the page's "SM resource control"), process-wide.  0 restores "all";
+ * values above the device's count are clamped.  Returns the previous value. */
+int fp8_set_num_cus(int num_cus);
+int fp8_get_num_cus(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* fp8_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GEMM_H */

@@ -1,0 +1,157 @@
+"""Helpers for the GPU parity tests: seeded inputs quantised by the CPU oracle,
+uploads, sentinel/canary-guarded output buffers, and comparison against the
+oracle at the bar |gpu - ref| <= 8e-3 |ref| + 1e-2 rms(ref)."""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+from fp8_block_scaled_04_amd import binding, synth
+
+SENTINEL = 0x5A5A     # bf16 bit pattern pre-filled where the kernel must not write
+CANARY = 0x3C3C       # guard band before and after every output buffer
+GUARD = 4096          # guard elements on each side (8 KiB)
+RTOL, ATOL_RMS = 8e-3, 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a ROCm device"
+    binding.lib()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def kg_of(k):
+    return (k + 127) // 128
+
+
+def ld_of(rows):
+    return max(4, (rows + 3) // 4 * 4)
+
+
+def sa_mn_major(sa_logical, ld=None):
+    """Logical [rows][KG] LHS scales -> MN-major [KG][ld] (padding 0)."""
+    rows, kg = sa_logical.shape
+    ld = ld or ld_of(rows)
+    out = np.zeros((kg, ld), np.float32)
+    out[:, :rows] = sa_logical.T
+    return out
+
+
+class Guarded:
+    """A uint16 device buffer with canary bands around a [shape] view that is
+    pre-filled with the sentinel."""
+
+    def __init__(self, shape, fill=SENTINEL):
+        self.shape = tuple(shape)
+        self.count = int(np.prod(self.shape))
+        host = np.full(self.count + 2 * GUARD, CANARY, np.uint16)
+        host[GUARD:GUARD + self.count] = fill
+        self.buf = dev(host.view(np.int16))
+        self.view = self.buf[GUARD:GUARD + self.count].view(self.shape).view(torch.bfloat16)
+
+    def result(self):
+        torch.cuda.synchronize()
+        host = self.buf.cpu().numpy().view(np.uint16)
+        assert np.all(host[:GUARD] == CANARY), "write below the output buffer"
+        assert np.all(host[GUARD + self.count:] == CANARY), "write above the output buffer"
+        return host[GUARD:GUARD + self.count].reshape(self.shape)
+
+
+def assert_close(gpu_bits, ref_bits, what=""):
+    ok, worst, rms = oracle.tolerance_check(gpu_bits, ref_bits, RTOL, ATOL_RMS)
+    assert ok, f"{what}: worst |err|/bound = {worst:.3f} (rms {rms:.4g})"
+    return worst
+
+
+# ---- quantised operands (the oracle's casts: no GPU value feeds the oracle) ---
+def dense_case(m, n, k, seed=0, outliers=False):
+    x, w = synth.dense_operands(m, n, k, seed=seed, outliers=outliers)
+    qa, sa = oracle.cast_1x128(x)
+    qb, sb = oracle.cast_128x128(w)
+    return qa, sa, qb, sb
+
+
+def run_dense(qa, sa, qb, sb, use_workspace=True, guarded=True):
+    m, k = qa.shape
+    n = qb.shape[0]
+    out = Guarded((m, n))
+    ws = None
+    if use_workspace:
+        nbytes = binding.fp8_gemm_workspace_bytes(m, n, k)
+        if nbytes:
+            ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    binding.fp8_gemm_nt(dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb), out.view, workspace=ws)
+    return out.result()
+
+
+def contiguous_case(sizes, n, k, seed=0):
+    x, w, m_idx = synth.contiguous_operands(sizes, n, k, seed=seed)
+    qa, sa = oracle.cast_1x128(x)
+    G = len(sizes)
+    qb = np.empty((G, n, k), np.uint8)
+    sb = np.empty((G, (n + 127) // 128, kg_of(k)), np.float32)
+    for g in range(G):
+        qb[g], sb[g] = oracle.cast_128x128(w[g])
+    return qa, sa, qb, sb, m_idx
+
+
+def run_contiguous(qa, sa, qb, sb, m_idx):
+    M = qa.shape[0]
+    n = qb.shape[1]
+    out = Guarded((M, n))
+    binding.fp8_grouped_gemm_contiguous(dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb), out.view,
+                                        dev(m_idx.astype(np.int32)))
+    return out.result()
+
+
+def masked_case(G, max_m, n, k, counts, seed=0):
+    """Operands for the masked layout; rows at or past each count hold
+    random bytes in both the codes and the scale bit patterns."""
+    x, w = synth.masked_operands(G, max_m, n, k, seed=seed)
+    kg = kg_of(k)
+    qa = np.empty((G, max_m, k), np.uint8)
+    sa = np.empty((G, max_m, kg), np.float32)
+    qb = np.empty((G, n, k), np.uint8)
+    sb = np.empty((G, (n + 127) // 128, kg), np.float32)
+    for g in range(G):
+        qa[g], sa[g] = oracle.cast_1x128(x[g])
+        qb[g], sb[g] = oracle.cast_128x128(w[g])
+    junk = synth.garbage_bytes(qa.size + sa.size * 4, seed=seed)
+    ja = junk[:qa.size].reshape(qa.shape)
+    js = junk[qa.size:].view(np.float32).reshape(sa.shape)
+    for g in range(G):
+        c = int(counts[g])
+        qa[g, c:] = ja[g, c:]
+        sa[g, c:] = js[g, c:]
+    return qa, sa, qb, sb
+
+
+def run_masked(qa, sa, qb, sb, counts):
+    G, max_m, k = qa.shape
+    n = qb.shape[1]
+    ld = ld_of(max_m)
+    sa_dev = np.stack([sa_mn_major(sa[g], ld) for g in range(G)])
+    out = Guarded((G, max_m, n))
+    binding.fp8_grouped_gemm_masked(dev(qa), dev(sa_dev), dev(qb), dev(sb), out.view,
+                                    dev(np.asarray(counts, np.int32)))
+    return out.result()
+
+
+def sample_points(rows, n, count, seed):
+    """Output coordinates that cover every 16-row and 16-column sub-tile
+    boundary class plus the last row/column, then random ones."""
+    rng = np.random.default_rng(seed)
+    r = list(range(min(rows, 20))) + list(range(max(0, rows - 20), rows))
+    c = list(range(min(n, 20))) + list(range(max(0, n - 20), n))
+    rr = np.concatenate([np.array(r), rng.integers(0, rows, count)])
+    cc = np.concatenate([np.array(c)[rng.integers(0, len(c), len(r))], rng.integers(0, n, count)])
+    return rr.astype(np.int64), cc.astype(np.int64)

@@ -1,0 +1,91 @@
+"""CPU-only checks of the C-ABI library: it loads, exports every function
+include/fp8gemm.h declares, and rejects bad arguments on the host before any
+launch.  No call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp8_block_scaled_04_amd import binding, build
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(build.LIB):
+        build.build()
+    return binding.lib()
+
+
+def test_exports_every_declared_function(lib):
+    names = binding.header_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(binding._SIGNATURES)
+
+
+def test_status_strings(lib):
+    assert binding.status_string(0) == "ok"
+    assert "invalid" in binding.status_string(-1)
+    assert "unsupported" in binding.status_string(-2)
+    assert "launch" in binding.status_string(-3)
+    assert "unknown" in binding.status_string(7)
+
+
+def test_host_validation_paths(lib):
+    g = lib.fp8_gemm_nt
+    # null pointers
+    assert g(None, None, 4, None, None, None, 4, 8, 128, None, 0, None) == binding.FP8G_EINVAL
+    # negative sizes
+    assert g(None, None, 4, None, None, None, -1, 8, 128, None, 0, None) == binding.FP8G_EINVAL
+    # K not a multiple of 128, N not a multiple of 8, K too large
+    assert g(None, None, 4, None, None, None, 4, 8, 100, None, 0, None) == binding.FP8G_EUNSUPPORTED
+    assert g(None, None, 4, None, None, None, 4, 12, 128, None, 0, None) == binding.FP8G_EUNSUPPORTED
+    assert g(None, None, 4, None, None, None, 4, 8, 128 * 513, None, 0, None) == binding.FP8G_EUNSUPPORTED
+    # zero-sized problems are no-ops
+    assert g(None, None, 4, None, None, None, 0, 8, 128, None, 0, None) == binding.FP8G_OK
+    assert g(None, None, 4, None, None, None, 4, 0, 128, None, 0, None) == binding.FP8G_OK
+    c = lib.fp8_grouped_gemm_contiguous
+    assert c(None, None, 128, None, None, None, None, 100, 8, 128, 2, None, 0, None) == binding.FP8G_EUNSUPPORTED
+    assert c(None, None, 128, None, None, None, None, 128, 8, 128, 2, None, 0, None) == binding.FP8G_EINVAL
+    assert c(None, None, 128, None, None, None, None, 0, 8, 128, 2, None, 0, None) == binding.FP8G_OK
+    mk = lib.fp8_grouped_gemm_masked
+    assert mk(None, None, 4, None, None, None, None, 2, 4, 8, 128, None, 0, None) == binding.FP8G_EINVAL
+    assert mk(None, None, 4, None, None, None, None, 0, 4, 8, 128, None, 0, None) == binding.FP8G_OK
+    assert mk(None, None, 4, None, None, None, None, -1, 4, 8, 128, None, 0, None) == binding.FP8G_EINVAL
+    t = lib.fp8_cast_per_token_group
+    assert t(None, 0, 4, 128, None, None, 4, None) == binding.FP8G_EINVAL
+    assert t(None, 5, 4, 128, None, None, 4, None) == binding.FP8G_EINVAL
+    assert t(None, 0, 4, 12, None, None, 4, None) == binding.FP8G_EUNSUPPORTED
+    b = lib.fp8_cast_per_block
+    assert b(None, 4, 128, None, None, None) == binding.FP8G_EINVAL
+    assert b(None, 4, 6, None, None, None) == binding.FP8G_EUNSUPPORTED
+
+
+def test_cu_limit_setter(lib):
+    prev = binding.fp8_set_num_cus(17)
+    try:
+        assert binding.fp8_set_num_cus(3) == 17
+        assert 1 <= binding.fp8_get_num_cus() <= 3
+    finally:
+        binding.fp8_set_num_cus(prev)
+
+
+def test_oracle_and_gpu_path_share_nothing():
+    """The oracle is test infrastructure: the package never imports it, it
+    never imports the package, and no source file is shared."""
+    pkg = os.path.join(ROOT, "fp8_block_scaled_04_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle\b", text, re.M), f
+                assert "fp8_oracle" not in text, f
+    for f in os.listdir(os.path.join(ROOT, "oracle")):
+        if f.endswith((".py", ".cpp")):
+            text = open(os.path.join(ROOT, "oracle", f)).read()
+            assert "fp8_block_scaled_04_amd" not in text, f
+            assert "fp8gemm" not in text and "hip" not in text.lower().replace("ship", ""), f

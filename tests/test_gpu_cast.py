@@ -1,0 +1,106 @@
+"""GPU parity of the FP8 casts: codes and scales must equal the CPU oracle's
+bit for bit (per-token-group cast: kwkr.cn usage article §3.1/§4.2; 128x128
+block scales: "DeepSeek open-source week, day 3: DeepGEMM", "Basic usage")."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_04_amd import binding, synth
+from _gpu import dev, kg_of, ld_of, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_cast_1x128(x_host, ld=None):
+    m, k = x_host.shape
+    ld = ld or ld_of(m)
+    if x_host.dtype == np.uint16:
+        xd = dev(x_host.view(np.int16)).view(torch.bfloat16)
+    else:
+        xd = dev(x_host)
+    q = torch.full((m, k), 0xEE, dtype=torch.uint8, device="cuda")
+    s = torch.full((kg_of(k), ld), -7.0, dtype=torch.float32, device="cuda")
+    binding.fp8_cast_per_token_group(xd, q, s)
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), s.cpu().numpy()
+
+
+@pytest.mark.parametrize("m,k", [(1, 128), (16, 128), (37, 1000), (64, 7168), (300, 2048), (4096, 7168)])
+def test_cast_1x128_f32_bit_exact(m, k):
+    require_gpu()
+    say(f"cast_1x128 f32 m={m} k={k}")
+    x = synth.normal_f32(0, synth.S_LHS, (m, k))
+    if m > 8:
+        x[3, :] = 0.0                      # all-zero row -> scale 1, codes 0
+        x[5, :128] = 0.0                   # one zero group
+        x[7, 9] = -0.0
+    qr, sr = oracle.cast_1x128(x)
+    q, s = gpu_cast_1x128(x)
+    assert np.array_equal(q, qr)
+    assert np.array_equal(s[:, :m].view(np.uint32), sr.T.view(np.uint32))
+    assert np.all(s[:, m:] == -7.0)        # padding columns of the scales untouched
+
+
+@pytest.mark.parametrize("m,k", [(5, 256), (128, 7168)])
+def test_cast_1x128_bf16_bit_exact(m, k):
+    require_gpu()
+    say(f"cast_1x128 bf16 m={m} k={k}")
+    x = synth.normal_f32(1, synth.S_LHS, (m, k)) * np.float32(3.0)
+    bits = torch.tensor(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    qr, sr = oracle.cast_1x128(bits)
+    q, s = gpu_cast_1x128(bits)
+    assert np.array_equal(q, qr)
+    assert np.array_equal(s[:, :m].view(np.uint32), sr.T.view(np.uint32))
+
+
+def test_cast_every_code_and_midpoint():
+    """Each 128-group holds 448 (so the scale is exactly 1) and then codes,
+    midpoints between neighbouring codes and their float neighbours: the
+    conversion must round to nearest-even exactly like the oracle."""
+    require_gpu()
+    t = oracle.e4m3_table()
+    vals = []
+    for c in range(0x7E):
+        mid = np.float32((t[c] + t[c + 1]) / 2)
+        vals += [np.float32(t[c]), mid, np.nextafter(mid, np.float32(0)), np.nextafter(mid, np.float32(1000))]
+    vals = np.array(vals, np.float32)
+    vals = np.concatenate([vals, -vals])
+    per_row = 127
+    rows = (vals.size + per_row - 1) // per_row
+    x = np.zeros((rows, 128), np.float32)
+    x[:, 0] = 448.0
+    flat = np.zeros(rows * per_row, np.float32)
+    flat[:vals.size] = vals
+    x[:, 1:] = flat.reshape(rows, per_row)
+    qr, sr = oracle.cast_1x128(x)
+    assert np.all(sr == 1.0)
+    q, s = gpu_cast_1x128(x)
+    assert np.array_equal(q, qr)
+    assert np.all(s[:, :rows] == 1.0)
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (130, 200), (300, 1000), (2112, 7168)])
+def test_cast_128x128_bit_exact(n, k):
+    require_gpu()
+    say(f"cast_128x128 n={n} k={k}")
+    w = synth.normal_f32(0, synth.S_RHS, (n, k))
+    if n > 128:
+        w[128:, :] *= np.float32(100.0)
+    qr, sr = oracle.cast_128x128(w)
+    q = torch.full((n, k), 0xEE, dtype=torch.uint8, device="cuda")
+    s = torch.zeros(sr.shape, dtype=torch.float32, device="cuda")
+    binding.fp8_cast_per_block(dev(w), q, s)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.cpu().numpy(), qr)
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), sr.view(np.uint32))
+
+
+def test_cast_rejects_bad_shapes():
+    require_gpu()
+    x = torch.zeros((4, 100), dtype=torch.float32, device="cuda")   # k % 8 != 0
+    q = torch.empty((4, 100), dtype=torch.uint8, device="cuda")
+    s = torch.empty((1, 4), dtype=torch.float32, device="cuda")
+    with pytest.raises(binding.Fp8GemmError) as e:
+        binding.fp8_cast_per_token_group(x, q, s)
+    assert e.value.status == binding.FP8G_EUNSUPPORTED

@@ -1,0 +1,151 @@
+"""GPU parity of the dense block-scaled FP8 NT GEMM against the CPU oracle
+("DeepSeek open-source week, day 3: DeepGEMM": "Basic usage" operands and
+scales, "Core features" two-level accumulation, BF16 output).
+
+Every output is compared at small and medium sizes; at the full workload
+sizes, sampled outputs are computed one by one by the oracle.  Output
+buffers carry canary bands, so stray stores fail the test."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_block_scaled_04_amd import binding
+from _gpu import (assert_close, dense_case, dev, require_gpu, run_dense, sa_mn_major, sample_points,
+                  say, Guarded)
+
+pytestmark = pytest.mark.gpu
+
+SMALL_SHAPES = [(1, 8, 128), (16, 64, 256), (63, 136, 384), (64, 2112, 1280), (65, 256, 512),
+                (128, 264, 640), (129, 136, 384), (257, 520, 1280), (512, 384, 1024), (300, 1000, 2048)]
+
+
+@pytest.mark.parametrize("m,n,k", SMALL_SHAPES)
+def test_dense_every_output(m, n, k):
+    require_gpu()
+    say(f"dense every-output m={m} n={n} k={k}")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=m + n + k)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    for ws in (True, False):
+        got = run_dense(qa, sa, qb, sb, use_workspace=ws)
+        assert_close(got, ref, f"m={m} n={n} k={k} ws={ws}")
+
+
+def test_dense_k_tail_regression_shape():
+    """The K-tail failure shape of the jianying88 practice article (§6.1):
+    M = N = 6144, K = 1280, checked on sampled outputs."""
+    require_gpu()
+    m = n = 6144
+    k = 1280
+    qa, sa, qb, sb = dense_case(m, n, k, seed=61)
+    got = run_dense(qa, sa, qb, sb)
+    r, c = sample_points(m, n, 3000, seed=1)
+    assert_close(got[r, c], oracle.gemm_points(qa, sa, qb, sb, r, c), "6144x6144x1280")
+
+
+def test_dense_config0_full():
+    """m=64, n=2112, k=7168, seed 0: every output."""
+    require_gpu()
+    say("dense m=64 n=2112 k=7168 (every output)")
+    qa, sa, qb, sb = dense_case(64, 2112, 7168, seed=0)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    got = run_dense(qa, sa, qb, sb)
+    assert_close(got, ref, "64x2112x7168")
+    again = run_dense(qa, sa, qb, sb)
+    assert np.array_equal(got, again), "two runs differ"
+
+
+NK = [(4096, 7168), (7168, 2048), (24576, 1536), (7168, 16384)]
+
+
+@pytest.mark.parametrize("m", [64, 128, 4096])
+@pytest.mark.parametrize("n,k", NK)
+def test_dense_config1_sweep(m, n, k):
+    """The m x (n, k) sweep: m <= 128 every output, m = 4096 sampled."""
+    require_gpu()
+    say(f"dense sweep m={m} n={n} k={k}")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=0)
+    got = run_dense(qa, sa, qb, sb)
+    if m <= 128:
+        ref = oracle.gemm_nt(qa, sa, qb, sb)
+        assert_close(got, ref, f"{m}x{n}x{k}")
+    else:
+        r, c = sample_points(m, n, 4000, seed=m + n)
+        assert_close(got[r, c], oracle.gemm_points(qa, sa, qb, sb, r, c), f"{m}x{n}x{k} sampled")
+
+
+@pytest.mark.parametrize("m,n,k", [(8192, 8192, 8192), (16384, 7168, 16384)])
+def test_dense_config4_outliers_sampled(m, n, k):
+    """Large compute-bound shapes with 1% of elements scaled by 50."""
+    require_gpu()
+    say(f"dense large m={m} n={n} k={k} (outliers, sampled)")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=0, outliers=True)
+    got = run_dense(qa, sa, qb, sb)
+    r, c = sample_points(m, n, 3000, seed=4)
+    assert_close(got[r, c], oracle.gemm_points(qa, sa, qb, sb, r, c), f"{m}x{n}x{k} sampled")
+
+
+def test_dense_split_and_unsplit_agree_and_are_deterministic():
+    require_gpu()
+    qa, sa, qb, sb = dense_case(64, 1024, 4096, seed=5)
+    a = run_dense(qa, sa, qb, sb, use_workspace=True)
+    b = run_dense(qa, sa, qb, sb, use_workspace=True)
+    c = run_dense(qa, sa, qb, sb, use_workspace=False)
+    assert np.array_equal(a, b)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    assert_close(a, ref, "split")
+    assert_close(c, ref, "unsplit")
+
+
+def test_dense_cu_limit_does_not_change_results():
+    require_gpu()
+    qa, sa, qb, sb = dense_case(96, 512, 2048, seed=6)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    prev = binding.fp8_set_num_cus(16)
+    try:
+        got = run_dense(qa, sa, qb, sb)
+    finally:
+        binding.fp8_set_num_cus(prev)
+    assert_close(got, ref, "16 CUs")
+
+
+def test_dense_scale_linearity_on_gpu():
+    """Doubling every RHS scale doubles every output exactly (a power-of-two
+    scale commutes with every rounding on the way)."""
+    require_gpu()
+    qa, sa, qb, sb = dense_case(64, 256, 1024, seed=7)
+    a = run_dense(qa, sa, qb, sb)
+    b = run_dense(qa, sa, qb, sb * np.float32(2.0))
+    fa = oracle.bf16_bits_to_f64(a)
+    fb = oracle.bf16_bits_to_f64(b)
+    assert np.array_equal(fb, 2.0 * fa)
+
+
+def test_dense_rejects_bad_shapes_before_launch():
+    require_gpu()
+    lhs = torch.zeros((4, 200), dtype=torch.uint8, device="cuda")
+    rhs = torch.zeros((8, 200), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((2, 4), dtype=torch.float32, device="cuda")
+    sb = torch.zeros((1, 2), dtype=torch.float32, device="cuda")
+    out = Guarded((4, 8))
+    with pytest.raises(binding.Fp8GemmError) as e:
+        binding.fp8_gemm_nt(lhs, sa, rhs, sb, out.view)
+    assert e.value.status == binding.FP8G_EUNSUPPORTED
+    res = out.result()
+    assert np.all(res == 0x5A5A)
+    # misaligned pointer
+    lhs2 = torch.zeros((4 * 128 + 8,), dtype=torch.uint8, device="cuda")[8:].view(4, 128)
+    with pytest.raises(binding.Fp8GemmError) as e:
+        binding.fp8_gemm_nt(lhs2, sa[:1], rhs[:, :128].contiguous(), sb[:, :1].contiguous(), out.view)
+    assert e.value.status == binding.FP8G_EINVAL
+
+
+def test_dense_zero_rows_is_a_noop():
+    require_gpu()
+    lhs = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
+    rhs = torch.zeros((8, 128), dtype=torch.uint8, device="cuda")
+    sa = torch.zeros((1, 4), dtype=torch.float32, device="cuda")
+    sb = torch.zeros((1, 1), dtype=torch.float32, device="cuda")
+    out = torch.empty((0, 8), dtype=torch.bfloat16, device="cuda")
+    binding.fp8_gemm_nt(lhs, sa, rhs, sb, out)
+    torch.cuda.synchronize()

@@ -1,0 +1,104 @@
+"""GPU parity of the grouped GEMMs ("DeepSeek open-source week, day 3:
+DeepGEMM": the contiguous-layout kind for MoE prefill and the masked-layout
+kind for MoE decode).  Rows the kernel must not write keep the sentinel bit
+for bit; canary bands catch stores outside the output buffer."""
+import numpy as np
+import pytest
+
+import oracle
+from fp8_block_scaled_04_amd import synth
+from _gpu import (SENTINEL, assert_close, contiguous_case, masked_case, require_gpu, run_contiguous,
+                  run_masked, sample_points, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("sizes,n,k", [([128], 8, 128), ([128, 256, 384], 264, 512),
+                                       ([256, 128, 128, 512], 1000, 1024)])
+def test_contiguous_every_output(sizes, n, k):
+    require_gpu()
+    say(f"contiguous every-output sizes={sizes} n={n} k={k}")
+    qa, sa, qb, sb, m_idx = contiguous_case(sizes, n, k, seed=sum(sizes))
+    ref = np.full((qa.shape[0], n), SENTINEL, np.uint16)
+    oracle.gemm_contiguous(qa, sa, qb, sb, m_idx, ref)
+    got = run_contiguous(qa, sa, qb, sb, m_idx)
+    assert_close(got, ref, f"contiguous {sizes}")
+
+
+def test_contiguous_skipped_block_untouched():
+    require_gpu()
+    sizes = [256, 128, 256]
+    qa, sa, qb, sb, m_idx = contiguous_case(sizes, 136, 256, seed=9)
+    m_idx = m_idx.copy()
+    m_idx[256:384] = -1
+    ref = np.full((640, 136), SENTINEL, np.uint16)
+    oracle.gemm_contiguous(qa, sa, qb, sb, m_idx, ref)
+    got = run_contiguous(qa, sa, qb, sb, m_idx)
+    assert np.all(got[256:384] == SENTINEL)
+    valid = m_idx >= 0
+    assert_close(got[valid], ref[valid], "contiguous with a skipped block")
+
+
+def test_contiguous_config2_sampled():
+    """G=8, n=4096, k=7168, m_g = 128 * U{4..32} (seed 0)."""
+    require_gpu()
+    sizes = synth.contiguous_group_sizes(8, seed=0)
+    say(f"contiguous G=8 sizes={list(sizes)} n=4096 k=7168 (sampled)")
+    qa, sa, qb, sb, m_idx = contiguous_case(sizes, 4096, 7168, seed=0)
+    got = run_contiguous(qa, sa, qb, sb, m_idx)
+    starts = np.concatenate([[0], np.cumsum(sizes)])
+    for g in range(8):
+        lo, hi = starts[g], starts[g + 1]
+        r, c = sample_points(hi - lo, 4096, 500, seed=g)
+        want = oracle.gemm_points(qa[lo:hi], sa[lo:hi], qb[g], sb[g], r, c)
+        assert_close(got[lo + r, c], want, f"expert {g}")
+
+
+@pytest.mark.parametrize("G,max_m,n,k,counts", [
+    (3, 64, 136, 256, [0, 17, 64]),
+    (4, 256, 264, 512, [1, 255, 256, 129]),
+    (2, 300, 128, 384, [300, 33]),
+])
+def test_masked_every_output(G, max_m, n, k, counts):
+    require_gpu()
+    say(f"masked every-output G={G} max_m={max_m} n={n} k={k} counts={counts}")
+    qa, sa, qb, sb = masked_case(G, max_m, n, k, counts, seed=G + n)
+    ref = np.full((G, max_m, n), SENTINEL, np.uint16)
+    oracle.gemm_masked(qa, sa, qb, sb, np.array(counts, np.int32), ref)
+    got = run_masked(qa, sa, qb, sb, counts)
+    for g, c in enumerate(counts):
+        assert np.all(got[g, c:] == SENTINEL), f"group {g} wrote past its count"
+    valid = np.concatenate([got[g, :c].ravel() for g, c in enumerate(counts)])
+    want = np.concatenate([ref[g, :c].ravel() for g, c in enumerate(counts)])
+    assert_close(valid, want, "masked")
+
+
+def test_masked_counts_are_clamped():
+    require_gpu()
+    G, max_m, n, k = 2, 64, 64, 128
+    qa, sa, qb, sb = masked_case(G, max_m, n, k, [64, 0], seed=3)
+    ref = np.full((G, max_m, n), SENTINEL, np.uint16)
+    oracle.gemm_masked(qa, sa, qb, sb, np.array([999, -5], np.int32), ref)
+    got = run_masked(qa, sa, qb, sb, [999, -5])
+    assert np.all(got[1] == SENTINEL)
+    assert_close(got[0], ref[0], "clamped count")
+
+
+def test_masked_config3_sampled():
+    """G=16, max_m=256, n=4096, k=7168, counts ~ U[0, 256] (seed 0); rows
+    past each count hold random bytes (NaN codes and NaN/Inf scales
+    included) and must neither affect nor receive output."""
+    require_gpu()
+    G, max_m, n, k = 16, 256, 4096, 7168
+    counts = synth.masked_counts(G, max_m, seed=0)
+    say(f"masked G=16 max_m=256 n=4096 k=7168 counts={list(counts)} (sampled)")
+    qa, sa, qb, sb = masked_case(G, max_m, n, k, counts, seed=0)
+    got = run_masked(qa, sa, qb, sb, counts)
+    for g in range(G):
+        c = int(counts[g])
+        assert np.all(got[g, c:] == SENTINEL), f"group {g} wrote past its count"
+        if c == 0:
+            continue
+        r, c_ = sample_points(c, n, 300, seed=g)
+        want = oracle.gemm_points(qa[g], sa[g], qb[g], sb[g], r, c_)
+        assert_close(got[g][r, c_], want, f"group {g}")

@@ -1,0 +1,273 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-scaled FP8 GEMM path on one MI355X.
+
+Default workload: the dense FP8 NT GEMM sweep m in {64, 128, 4096} x (n, k) in
+{(4096, 7168), (7168, 2048), (24576, 1536), (7168, 16384)}, 1x128 LHS and
+128x128 RHS FP32 block scales, BF16 output.  One step is one pass of the whole
+hot path over every shape: the per-token-group cast of the fp32 activations
+(x -> E4M3 codes + scales) followed by the GEMM.  Weights are quantised once,
+before timing, by the 128x128 block cast.  Inputs are seeded synthetic
+N(0, 1) data, resident in HBM before the timed region; every shape keeps
+enough rotated copies of its buffers that at least 1 GiB is touched between
+two uses of the same copy (4x the 256 MB Infinity Cache).
+
+Prints one JSON line.  `value` is the sweep's total GEMM FLOP divided by the
+measured step time (cast included).  `roofline` describes the kernel that
+takes the most time: algorithmic FLOP (or bytes) per launch divided by its
+mean launch duration from HIP events on the launch stream.  `cpu_baseline`
+times the CPU oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 GEMM TFLOPS (large M) and HBM GB/s (M<=256) at 1 MI355X, % of roofline"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+RIDGE = PEAK_FP8_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per byte
+ROTATE_BYTES = 1 << 30
+
+SWEEP_NK = [(4096, 7168), (7168, 2048), (24576, 1536), (7168, 16384)]
+WORKLOADS = {
+    "sweep": [(m, n, k) for m in (64, 128, 4096) for (n, k) in SWEEP_NK],
+    "cfg0": [(64, 2112, 7168)],
+    "large": [(8192, 8192, 8192), (16384, 7168, 16384)],
+}
+DESCRIPTION = {
+    "sweep": ("dense FP8 E4M3 NT GEMM sweep m in {64,128,4096} x (n,k) in {(4096,7168),(7168,2048),"
+              "(24576,1536),(7168,16384)}; 1x128 LHS / 128x128 RHS FP32 block scales; BF16 out; "
+              "step = per-token-group cast of fp32 activations + GEMM for every shape"),
+    "cfg0": "dense FP8 E4M3 NT GEMM m=64 n=2112 k=7168; step = activation cast + GEMM",
+    "large": ("dense FP8 E4M3 NT GEMM m=n=k=8192 and m=16384 n=7168 k=16384, 1% x50 outliers; "
+              "step = activation cast + GEMM"),
+}
+
+
+def algorithmic(m, n, k):
+    """FLOP and HBM bytes the GEMM must move: A, B, both scale tensors, the
+    BF16 output (padding, LDS traffic and split-K scratch not counted)."""
+    kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+    flop = 2.0 * m * n * k
+    nbytes = m * k + n * k + m * kg * 4 + nb * kg * 4 + m * n * 2
+    return flop, nbytes
+
+
+def cast_bytes(m, k):
+    kg = math.ceil(k / 128)
+    return m * k * 4 + m * k + m * kg * 4
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="sweep", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128, help="rows per shape in the oracle sample")
+    ap.add_argument("--shape", action="append", default=[],
+                    help="m,n,k to time instead of the workload's shapes (repeatable)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the path shards by N or by expert with no exchange inside the GEMM; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from fp8_block_scaled_04_amd import binding, synth
+
+    assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    torch.cuda.set_device(0)
+    binding.lib()
+    shapes = WORKLOADS[args.workload]
+    if args.shape:
+        shapes = [tuple(int(v) for v in sh.split(",")) for sh in args.shape]
+        DESCRIPTION[args.workload] = "custom shapes (not the default workload); step = activation cast + GEMM"
+    outliers = args.workload == "large"
+    stream = torch.cuda.current_stream()
+
+    # ---- inputs: generate, upload, quantise weights, rotate ----------------
+    t0 = time.time()
+    host = {}
+    cases = []
+    for (m, n, k) in shapes:
+        key = (m, k)
+        if key not in host:
+            x = synth.normal_f32(0, synth.S_LHS, (m, k))
+            if outliers:
+                x = synth.with_outliers(x, 0, synth.S_OUT_LHS)
+            host[key] = x
+        if (n, k) not in host:
+            w = synth.normal_f32(0, synth.S_RHS, (n, k))
+            if outliers:
+                w = synth.with_outliers(w, 0, synth.S_OUT_RHS)
+            host[(n, k)] = w
+    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    for (m, n, k) in shapes:
+        kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+        ld = max(4, (m + 3) // 4 * 4)
+        x_d = torch.from_numpy(host[(m, k)]).cuda()
+        w_d = torch.from_numpy(host[(n, k)]).cuda()
+        qb0 = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        sb0 = torch.empty((nb, kg), dtype=torch.float32, device="cuda")
+        binding.fp8_cast_per_block(w_d, qb0, sb0)
+        del w_d
+        foot = 4 * m * k + m * k + kg * ld * 4 + n * k + nb * kg * 4 + 2 * m * n
+        reps = int(min(64, max(1, math.ceil(ROTATE_BYTES / foot))))
+        ws_bytes = binding.fp8_gemm_workspace_bytes(m, n, k)
+        ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device="cuda") if ws_bytes else None
+        sets = []
+        for r in range(reps):
+            sets.append(dict(
+                x=x_d if r == 0 else x_d.clone(),
+                q=torch.empty((m, k), dtype=torch.uint8, device="cuda"),
+                s=torch.empty((kg, ld), dtype=torch.float32, device="cuda"),
+                qb=qb0 if r == 0 else qb0.clone(),
+                sb=sb0 if r == 0 else sb0.clone(),
+                out=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+            ))
+        flop, nbytes = algorithmic(m, n, k)
+        cases.append(dict(m=m, n=n, k=k, sets=sets, ws=ws, flop=flop, bytes=nbytes,
+                          cast_bytes=cast_bytes(m, k), ev=[]))
+    torch.cuda.synchronize()
+    print(f"[bench] device buffers ready ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)",
+          file=sys.stderr, flush=True)
+
+    def run_step(step, record):
+        for c in cases:
+            b = c["sets"][step % len(c["sets"])]
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e2 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+            binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=stream)
+            if record:
+                e1.record(stream)
+            binding.fp8_gemm_nt(b["q"], b["s"], b["qb"], b["sb"], b["out"], workspace=c["ws"], stream=stream)
+            if record:
+                e2.record(stream)
+                c["ev"].append((e0, e1, e2))
+
+    for s in range(args.warmup):
+        run_step(s, False)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for s in range(args.steps):
+        run_step(args.warmup + s, True)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    print(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall",
+          file=sys.stderr, flush=True)
+
+    total_flop = sum(c["flop"] for c in cases)
+    by_shape = []
+    for c in cases:
+        cast_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in c["ev"]]))
+        gemm_ms = float(np.mean([b.elapsed_time(d) for _, b, d in c["ev"]]))
+        c["gemm_ms"], c["cast_ms"] = gemm_ms, cast_ms
+        tflops = c["flop"] / (gemm_ms * 1e-3) / 1e12
+        gbs = c["bytes"] / (gemm_ms * 1e-3) / 1e9
+        bound = "mfma" if c["flop"] / c["bytes"] >= RIDGE else "hbm"
+        frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
+        by_shape.append(dict(m=c["m"], n=c["n"], k=c["k"], gemm_us=round(gemm_ms * 1e3, 2),
+                             cast_us=round(cast_ms * 1e3, 2), tflops=round(tflops, 1), gbs=round(gbs, 1),
+                             bound=bound, frac=round(frac, 4),
+                             cast_gbs=round(c["cast_bytes"] / (cast_ms * 1e-3) / 1e9, 1)))
+    dom = max(cases, key=lambda c: c["gemm_ms"])
+    dom_bound = "mfma" if dom["flop"] / dom["bytes"] >= RIDGE else "hbm"
+    if dom_bound == "mfma":
+        achieved = dom["flop"] / (dom["gemm_ms"] * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s")
+    else:
+        achieved = dom["bytes"] / (dom["gemm_ms"] * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s")
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = f"fp8_gemm_nt m={dom['m']} n={dom['n']} k={dom['k']}"
+    roof["per_launch"] = (f"{dom['flop']:.4g} FLOP" if dom_bound == "mfma" else f"{dom['bytes']:.4g} B")
+
+    small = [c for c in cases if c["m"] <= 256]
+    large = [c for c in cases if c["m"] > 256]
+    summary = {}
+    if small:
+        summary["small_m_gemm_gbs"] = round(sum(c["bytes"] for c in small) /
+                                            (sum(c["gemm_ms"] for c in small) * 1e-3) / 1e9, 1)
+    if large:
+        summary["large_m_gemm_tflops"] = round(sum(c["flop"] for c in large) /
+                                               (sum(c["gemm_ms"] for c in large) * 1e-3) / 1e12, 1)
+
+    result = {
+        "metric": METRIC,
+        "value": round(total_flop / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTION[args.workload], "shapes": [list(s) for s in shapes],
+                   "seed": 0, "rotated_sets": {f"{c['m']}x{c['n']}x{c['k']}": len(c["sets"]) for c in cases}},
+        "roofline": roof,
+        "summary": summary,
+        "by_shape": by_shape,
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(shapes, host, rows_per_shape):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    the first `rows_per_shape` rows of every shape, cast + GEMM, all host
+    threads.  Scaled to the metric's unit (TFLOP/s of GEMM work)."""
+    import oracle
+    threads = oracle.hardware_threads()
+    wq = {}
+    for (m, n, k) in shapes:
+        if (n, k) not in wq:
+            wq[(n, k)] = oracle.cast_128x128(host[(n, k)], nthreads=threads)  # offline weights: not timed
+    flop = 0.0
+    t = 0.0
+    for (m, n, k) in shapes:
+        r = min(m, rows_per_shape)
+        x = np.ascontiguousarray(host[(m, k)][:r])
+        qb, sb = wq[(n, k)]
+        t0 = time.perf_counter()
+        qa, sa = oracle.cast_1x128(x, nthreads=threads)
+        oracle.gemm_nt(qa, sa, qb, sb, nthreads=threads)
+        t += time.perf_counter() - t0
+        flop += 2.0 * r * n * k
+    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {rows_per_shape} rows (all rows if fewer) of every shape: cast + GEMM, "
+                      f"{flop / 2e9:.1f} G MAC in {t:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

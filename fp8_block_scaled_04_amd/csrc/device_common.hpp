@@ -48,16 +48,43 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// LDS swizzle of a [rows][128 B] tile: the 16-byte chunk c of row r is kept
-// at chunk position c ^ (r & 7), so the 8 rows read together by one pass of
-// a 16-byte-per-lane LDS read land in 8 different chunk columns.
-__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ (row & 7); }
+// LDS layout of an operand tile of 128-byte rows (one K group of FP8 codes
+// per row), in blocks of 16 rows (2 KB).  Row q of a block lives in 256-byte
+// line q & 7, half q >> 3, and its logical 16-byte chunk c sits at chunk
+// position c ^ (q & 7) of that half:
+//     byte(q, c) = 256 * (q & 7) + 128 * (q >> 3) + 16 * (c ^ (q & 7)).
+// An MFMA fragment read has lane l fetch row l & 15 at one chunk per 16-lane
+// group.  Measured on gfx950, the 16 lanes served together conflict when
+// rows 2i and 2i+1 share a 256-byte line (the plain 128-byte-row layout,
+// with any XOR swizzle, costs two cycles per read); with rows q and q+8
+// paired in a line the reads take one cycle.
+__device__ __forceinline__ int tile_byte(int q, int c) {
+  return 256 * (q & 7) + 128 * (q >> 3) + 16 * (c ^ (q & 7));
+}
 
-// Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes land at
-// lds_wave_base + 16 * i (gfx950 global_load_lds_dwordx4).
-__device__ __forceinline__ void copy16_to_lds(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc,
-      (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+// Inverse map used by the copies: the 16-byte slot i (0..63) of half h of a
+// 16-row block holds row tile_row(h, i) at logical chunk tile_chunk(h, i).
+__device__ __forceinline__ int tile_row(int h, int i) { return 4 * h + (i >> 4) + 8 * ((i >> 3) & 1); }
+__device__ __forceinline__ int tile_chunk(int h, int i) { return (i & 7) ^ (tile_row(h, i) & 7); }
+
+// 32-bit LDS address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(uintptr_t((const __attribute__((address_space(3))) void*)p));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes come from
+// sbase + voffset (a wave-uniform 64-bit base plus a per-lane 32-bit offset)
+// and land at LDS address lds_wave_base + 16 * i (gfx950
+// global_load_lds_dwordx4, LDS base in M0).  Issued as inline assembly so
+// that the compiler does not track it: the compiler would otherwise wait for
+// every outstanding copy before any LDS read it cannot prove disjoint, which
+// serialises the prefetch ring.  The callers therefore own the
+// synchronisation: wait_vmcnt<N>() retires the copies in issue order, then a
+// barrier publishes them to the workgroup.  M0 is written here; these kernels
+// use it for nothing else.
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voffset, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_wave_base), "v"(voffset), "s"(sbase) : "memory");
 }
 
 // Uniform (per-wave) value: keeps address arithmetic in scalar registers.

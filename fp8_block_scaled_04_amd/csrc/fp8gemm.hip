@@ -78,9 +78,11 @@ int check_ld(int64_t ld, int64_t rows) {
 // Kernel shapes (BM tokens x BN outputs per workgroup, wave grid, LDS stages):
 //   kDenseM64   64 x 128, waves 1x4, 4 stages  (m <= 64)
 //   kDenseM128 128 x 128, waves 2x2, 3 stages  (m <= 128)
-//   kDenseBig  256 x 128, waves 2x2, 3 stages  (m > 128)
+//   kDenseBig  256 x 256, waves 4x2 (two per SIMD), 2 stages  (m > 128)
 // A wave's accumulator tile is at most 128 x 64 (128 VGPRs): the promotion
-// FMAs need their accumulators in the 256 architectural VGPRs.
+// FMAs need their accumulators in architectural VGPRs, and two waves per SIMD
+// (eight per workgroup) share the SIMD's registers so that one wave's LDS
+// and barrier waits are covered by the other's MFMAs.
 // When the tile count would leave CUs idle, K is split across workgroups and
 // the partials are summed in a fixed order.
 enum DenseKind { kDenseM64 = 0, kDenseM128 = 1, kDenseBig = 2 };
@@ -93,7 +95,7 @@ DenseConfig dense_config(int m, int n, int k, bool allow_split) {
   DenseConfig c{};
   if (m <= 64) { c.kind = kDenseM64; c.bm = 64; c.bn = 128; }
   else if (m <= 128) { c.kind = kDenseM128; c.bm = 128; c.bn = 128; }
-  else { c.kind = kDenseBig; c.bm = 256; c.bn = 128; }
+  else { c.kind = kDenseBig; c.bm = 256; c.bn = 256; }
   c.tiles_m = int(cdiv(m, c.bm));
   c.tiles_n = int(cdiv(n, c.bn));
   const int kg = k / 128;
@@ -117,7 +119,8 @@ size_t dense_workspace(const DenseConfig& c, int m, int n) {
 
 template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT>
 void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT>), dim3(unsigned(grid)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT>), dim3(unsigned(grid)), dim3(64 * WMW * WNW), 0, s,
+                     p);
 }
 
 template <bool SPLIT>
@@ -125,7 +128,7 @@ void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
   switch (kind) {
     case kDenseM64: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
     case kDenseM128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
-    default: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
+    default: launch_gemm<256, 256, 4, 2, 2, kDense, SPLIT>(p, grid, s); break;
   }
 }
 
@@ -249,7 +252,7 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] masked G=%d max_m=%d n=%d k=%d grid=%lld\n", num_groups, max_m, n, k,
                  (long long)grid);
-  launch_gemm<256, 128, 2, 2, 3, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
+  launch_gemm<256, 128, 4, 1, 3, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
   return launched("masked gemm");
 }
 

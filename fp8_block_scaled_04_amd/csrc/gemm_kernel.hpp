@@ -48,15 +48,15 @@ struct GemmParams {
   int splits, groups_per_split;
 };
 
-// Reads this lane's 32-byte K slice of row `row` of a swizzled [rows][128 B]
-// LDS tile: lane l supplies row (l & 15) of a 16-row fragment and K bytes
-// [32 * (l >> 4), +32).  The same slice assignment is used for both MFMA
-// operands, so the pairing of K elements is consistent.
-__device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lane) {
-  const int c0 = 2 * (lane >> 4);
-  const uint8_t* base = tile + row * kRowBytes;
-  const v4i x = *reinterpret_cast<const v4i*>(base + 16 * swz(row, c0));
-  const v4i y = *reinterpret_cast<const v4i*>(base + 16 * swz(row, c0 + 1));
+// Loads this lane's 32-byte K slice of one 16-row MFMA fragment from an LDS
+// tile laid out by tile_byte().  Lane l supplies row (l & 15) and K bytes
+// [32 * (l >> 4), +32), i.e. logical 16-byte chunks c0 = 2 * (l >> 4) and
+// c0 + 1; p0 and p1 point at where the layout put those two chunks.  Both
+// MFMA operands use the same slice assignment, so K elements pair up
+// consistently.
+__device__ __forceinline__ v8i lds_frag(const uint8_t* p0, const uint8_t* p1) {
+  const v4i x = *reinterpret_cast<const v4i*>(p0);
+  const v4i y = *reinterpret_cast<const v4i*>(p1);
   v8i r;
   r[0] = x[0]; r[1] = x[1]; r[2] = x[2]; r[3] = x[3];
   r[4] = y[0]; r[5] = y[1]; r[6] = y[2]; r[7] = y[3];
@@ -64,7 +64,7 @@ __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int lane)
 }
 
 // Waits until at most `newer` stages of copies issued after the current one
-// are still in flight (`copies` per stage per wave), then barriers.
+// are still in flight (`copies` per stage per wave).
 template <int STAGES, int COPIES>
 __device__ __forceinline__ void wait_stage(int newer) {
   if constexpr (STAGES >= 3) {
@@ -79,24 +79,114 @@ __device__ __forceinline__ void wait_stage(int newer) {
   wait_vmcnt<0>();
 }
 
+// Promotion of one 16x16 product: acc += scale * partial (one FMA per output).
+__device__ __forceinline__ void promote(v4f& acc, const v4f& part, float scale) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[r] = fmaf(part[r], scale, acc[r]);
+}
+
+// Per-lane LDS pointers of a wave's fragments in ring slot 0: chunk pointers
+// for its first 16-row LHS and RHS fragments and its LHS-scale entry.  Later
+// fragments sit 16 rows (2048 B) further on, later slots a whole tile on;
+// both are compile-time offsets.
+struct FragPtrs {
+  const uint8_t* a0;
+  const uint8_t* a1;
+  const uint8_t* b0;
+  const uint8_t* b1;
+  const float* s;
+};
+
+// One K group of a wave's TN x TM sub-tiles, read from ring slot SLOT.  The
+// operand with fewer fragments is held in registers, the other is streamed
+// one fragment ahead.  Each MFMA is issued before the promotion of the
+// previous product, so the promotion FMAs run while the next MFMA occupies
+// the matrix core.
+template <int TM, int TN, int A_SLOT, int B_SLOT, int S_SLOT>
+__device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs& f, float sbv) {
+  constexpr int FRAG = 16 * kRowBytes;
+  auto afrag = [&](int j) { return lds_frag(f.a0 + A_SLOT + j * FRAG, f.a1 + A_SLOT + j * FRAG); };
+  auto bfrag = [&](int i) { return lds_frag(f.b0 + B_SLOT + i * FRAG, f.b1 + B_SLOT + i * FRAG); };
+  auto ascale = [&](int j) { return f.s[S_SLOT / 4 + 16 * j] * sbv; };
+  if constexpr (TN <= TM) {
+    v8i bf[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) bf[i] = bfrag(i);
+    v8i a_cur = afrag(0);
+    float s_cur = ascale(0);
+    v4f prev = {0.f, 0.f, 0.f, 0.f};
+    float prev_s = 0.f;
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      v8i a_next = a_cur;
+      float s_next = s_cur;
+      if (j + 1 < TM) {
+        a_next = afrag(j + 1);
+        s_next = ascale(j + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < TN; ++i) {
+        const v4f pr = mfma16x16x128(bf[i], a_cur);
+        const int t = j * TN + i;
+        if (t > 0) promote(acc[(t - 1) % TN][(t - 1) / TN], prev, prev_s);
+        prev = pr;
+        prev_s = s_cur;
+      }
+      a_cur = a_next;
+      s_cur = s_next;
+    }
+    promote(acc[TN - 1][TM - 1], prev, prev_s);
+  } else {
+    v8i af[TM];
+    float sc[TM];
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      af[j] = afrag(j);
+      sc[j] = ascale(j);
+    }
+    v8i b_cur = bfrag(0);
+    v4f prev = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      v8i b_next = b_cur;
+      if (i + 1 < TN) b_next = bfrag(i + 1);
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const v4f pr = mfma16x16x128(b_cur, af[j]);
+        const int t = i * TM + j;
+        if (t > 0) promote(acc[(t - 1) / TM][(t - 1) % TM], prev, sc[(t - 1) % TM]);
+        prev = pr;
+      }
+      b_cur = b_next;
+    }
+    promote(acc[TN - 1][TM - 1], prev, sc[TM - 1]);
+  }
+}
+
+template <int N>
+struct Int { static constexpr int value = N; };
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT>
-__global__ void __launch_bounds__(256, 1) gemm_kernel(const GemmParams p) {
-  static_assert(WAVES_M * WAVES_N == 4, "four waves per workgroup");
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const GemmParams p) {
+  constexpr int NW = WAVES_M * WAVES_N;  // 4 waves: one per SIMD; 8 waves: two per SIMD
+  static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 sub-tiles");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range stays inside one RHS scale block");
-  static_assert(BM % 32 == 0 && BN % 32 == 0 && BM <= 256, "whole 8-row copies; scales in one copy");
+  static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM <= 256, "whole 1 KB copies; scales in one copy");
   static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
+  // LDS: [STAGES][BM][128 B] LHS tiles, then [STAGES][BN][128 B] RHS tiles,
+  // then [STAGES][BM] LHS scales, then the tile's RHS scale rows.
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes, S_BYTES = BM * 4;
-  constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
-  constexpr int A_COPIES = BM / 32, B_COPIES = BN / 32;  // 8-row copies per wave per stage
+  constexpr int A_REGION = 0, B_REGION = STAGES * A_BYTES, S_REGION = B_REGION + STAGES * B_BYTES;
+  constexpr int RING = S_REGION + STAGES * S_BYTES;
+  constexpr int A_COPIES = BM / (8 * NW), B_COPIES = BN / (8 * NW);  // 8-row copies per wave per stage
   static_assert((STAGES - 2) * (A_COPIES + B_COPIES) < 64, "vmcnt range");
-
   constexpr int SB_BLOCKS = (BN + 127) / 128;  // RHS scale blocks a tile touches
-  static_assert(STAGES * STAGE + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS");
+  static_assert(RING + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RING];
   __shared__ float sb_cache[SB_BLOCKS][kMaxGroups];
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -140,30 +230,36 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(const GemmParams p) {
   }
   const int niter = g_end - g_begin;
 
-  // ---- HBM -> LDS copies of one K group into ring slot `slot` --------------
-  const int cp_row = lane >> 3, cp_chunk = lane & 7;
-  auto issue = [&](int slot, int g) {
-    uint8_t* sA = smem + slot * STAGE;
-    uint8_t* sB = sA + A_BYTES;
-    uint8_t* sS = sB + B_BYTES;
+  // ---- HBM -> LDS copies: per-lane byte offsets are loop invariant --------
+  // Copy i of this wave fills 1 KB unit u = i * NW + wave of the tile, i.e.
+  // half u & 1 of 16-row block u >> 1: lane l fetches the row and logical
+  // chunk that tile_byte() places at byte 16 * l of that unit.
+  uint32_t a_off[A_COPIES], b_off[B_COPIES];
 #pragma unroll
-    for (int i = 0; i < A_COPIES; ++i) {
-      const int r0 = (i * 4 + wave) * 8;
-      const int r = r0 + cp_row;
-      const int grow = min(m0 + r, rows - 1);
-      copy16_to_lds(A + int64_t(grow) * p.k + g * kGroupK + 16 * swz(r, cp_chunk), sA + r0 * kRowBytes);
-    }
+  for (int i = 0; i < A_COPIES; ++i) {
+    const int u = i * NW + wave;
+    const int r = 16 * (u >> 1) + tile_row(u & 1, lane);
+    a_off[i] = uint32_t(min(m0 + r, rows - 1)) * uint32_t(p.k) + 16u * tile_chunk(u & 1, lane);
+  }
 #pragma unroll
-    for (int i = 0; i < B_COPIES; ++i) {
-      const int r0 = (i * 4 + wave) * 8;
-      const int r = r0 + cp_row;
-      const int grow = min(n0 + r, p.n - 1);
-      copy16_to_lds(B + int64_t(grow) * p.k + g * kGroupK + 16 * swz(r, cp_chunk), sB + r0 * kRowBytes);
-    }
-    if (wave == 0 && lane < BM / 4) {
-      const int t = min(m0 + 4 * lane, int(p.sa_ld) - 4);
-      copy16_to_lds(SA + int64_t(g) * p.sa_ld + t, sS);
-    }
+  for (int i = 0; i < B_COPIES; ++i) {
+    const int u = i * NW + wave;
+    const int r = 16 * (u >> 1) + tile_row(u & 1, lane);
+    b_off[i] = uint32_t(min(n0 + r, p.n - 1)) * uint32_t(p.k) + 16u * tile_chunk(u & 1, lane);
+  }
+  const uint32_t s_off = 4u * uint32_t(min(m0 + 4 * lane, int(p.sa_ld) - 4));
+  const uint32_t lds0 = uniform(int(lds_addr(smem)));
+  auto issue = [&](auto slot_tag, int g) {
+    constexpr int slot = decltype(slot_tag)::value;
+    const uint8_t* a_src = A + int64_t(g) * kGroupK;
+    const uint8_t* b_src = B + int64_t(g) * kGroupK;
+#pragma unroll
+    for (int i = 0; i < A_COPIES; ++i)
+      copy16_to_lds(a_src, a_off[i], lds0 + A_REGION + slot * A_BYTES + (i * NW + wave) * 1024);
+#pragma unroll
+    for (int i = 0; i < B_COPIES; ++i)
+      copy16_to_lds(b_src, b_off[i], lds0 + B_REGION + slot * B_BYTES + (i * NW + wave) * 1024);
+    if (wave == 0 && lane < BM / 4) copy16_to_lds(SA + int64_t(g) * p.sa_ld, s_off, lds0 + S_REGION + slot * S_BYTES);
   };
 
   v4f acc[TN][TM];
@@ -174,51 +270,45 @@ __global__ void __launch_bounds__(256, 1) gemm_kernel(const GemmParams p) {
 
   const int wrow_m = wm * WM, wrow_n = wn * WN;
   // The tile's RHS scale rows go to LDS once, so the K loop reads them
-  // without a global load (which would drain the copy queue to be consumed).
+  // without a global load.
 #pragma unroll
   for (int b = 0; b < SB_BLOCKS; ++b) {
     const int blk = min(n0 / 128 + b, p.nb - 1);
     for (int g = threadIdx.x; g < p.kg; g += blockDim.x) sb_cache[b][g] = SB[int64_t(blk) * p.kg + g];
   }
-  const float* sb_row = sb_cache[wrow_n / 128];
-  // sub-tiles of 16 tokens that hold at least one valid token
-  const int live_m = min(TM, max(0, (rows - m0 - wrow_m + 15) / 16));
+  const float* sb_row = sb_cache[wrow_n / 128] + g_begin;
+  // In the masked layout a wave whose tokens are all past the count skips
+  // the products (its copies still run: the ring is shared).
+  const bool wave_live = MODE != kMasked || m0 + wrow_m < rows;
 
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < niter) issue(s, g_begin + s);
+  // Fragment pointers of ring slot 0 (wave and fragment row offsets are
+  // multiples of 16, i.e. whole 2 KB blocks).
+  const int lr = lane & 15, c0 = 2 * (lane >> 4);
+  FragPtrs f;
+  f.a0 = smem + A_REGION + wrow_m * kRowBytes + tile_byte(lr, c0);
+  f.a1 = smem + A_REGION + wrow_m * kRowBytes + tile_byte(lr, c0 + 1);
+  f.b0 = smem + B_REGION + wrow_n * kRowBytes + tile_byte(lr, c0);
+  f.b1 = smem + B_REGION + wrow_n * kRowBytes + tile_byte(lr, c0 + 1);
+  f.s = reinterpret_cast<const float*>(smem + S_REGION) + wrow_m + lr;
 
-  for (int it = 0; it < niter; ++it) {
+  if (0 < niter) issue(Int<0>{}, g_begin);
+  if constexpr (STAGES > 2) if (1 < niter) issue(Int<1>{}, g_begin + 1);
+  if constexpr (STAGES > 3) if (2 < niter) issue(Int<2>{}, g_begin + 2);
+
+  auto step = [&](auto slot_tag, int it) {
+    constexpr int slot = decltype(slot_tag)::value;
     wait_stage<STAGES, A_COPIES + B_COPIES>(min(STAGES - 2, niter - 1 - it));
     wait_lgkmcnt0();
     block_barrier();
-    if (it + STAGES - 1 < niter) issue((it + STAGES - 1) % STAGES, g_begin + it + STAGES - 1);
-
-    const int slot = it % STAGES;
-    const uint8_t* sA = smem + slot * STAGE;
-    const uint8_t* sB = sA + A_BYTES;
-    const float* sS = reinterpret_cast<const float*>(sB + B_BYTES);
-    const float sbv = sb_row[g_begin + it];
-
-    v8i af[TM];
-    float sc[TM];
-#pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      af[j] = read_frag(sA, wrow_m + 16 * j + (lane & 15), lane);
-      sc[j] = sS[wrow_m + 16 * j + (lane & 15)] * sbv;
-    }
-#pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const v8i bf = read_frag(sB, wrow_n + 16 * i + (lane & 15), lane);
-#pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        if (MODE != kMasked || j < live_m) {
-          const v4f pr = mfma16x16x128(bf, af[j]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(pr[r], sc[j], acc[i][j][r]);
-        }
-      }
-    }
+    if (it + STAGES - 1 < niter) issue(Int<(slot + STAGES - 1) % STAGES>{}, g_begin + it + STAGES - 1);
+    if (wave_live)
+      group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES>(acc, f, sb_row[it]);
+  };
+  for (int it = 0; it < niter; it += STAGES) {
+    step(Int<0>{}, it);
+    if (it + 1 < niter) step(Int<1 % STAGES>{}, it + 1);
+    if constexpr (STAGES > 2) if (it + 2 < niter) step(Int<2 % STAGES>{}, it + 2);
+    if constexpr (STAGES > 3) if (it + 3 < niter) step(Int<3 % STAGES>{}, it + 3);
   }
 
   // ---- epilogue: lane holds n = col..col+3 of one token per sub-tile -------

@@ -12,10 +12,12 @@ enough rotated copies of its buffers that at least 1 GiB is touched between
 two uses of the same copy (4x the 256 MB Infinity Cache).
 
 Prints one JSON line.  `value` is the sweep's total GEMM FLOP divided by the
-measured step time (cast included).  `roofline` describes the kernel that
-takes the most time: algorithmic FLOP (or bytes) per launch divided by its
-mean launch duration from HIP events on the launch stream.  `cpu_baseline`
-times the CPU oracle on a bounded sample of the same workload.
+measured step time (cast included; the steps are bracketed by two events
+only).  Per-kernel durations come from a second phase that launches each
+kernel back to back between two events on the same stream.  `roofline`
+describes the kernel that takes the most time: algorithmic FLOP (or bytes)
+per launch divided by its mean launch duration.  `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -74,10 +76,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="sweep", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=128, help="rows per shape in the oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the oracle sample")
     ap.add_argument("--shape", action="append", default=[],
                     help="m,n,k to time instead of the workload's shapes (repeatable)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="run only a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--digest", action="store_true", help="print the GEMM kernel source digest and exit")
     args = ap.parse_args()
+    if args.digest:
+        print(kernel_source_digest())
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(the path shards by N or by expert with no exchange inside the GEMM; see the design notes)",
@@ -89,6 +97,9 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        copy_calibration(args.copy_bytes, args.steps)
+        return
     binding.lib()
     shapes = WORKLOADS[args.workload]
     if args.shape:
@@ -140,39 +151,36 @@ def main():
             ))
         flop, nbytes = algorithmic(m, n, k)
         cases.append(dict(m=m, n=n, k=k, sets=sets, ws=ws, flop=flop, bytes=nbytes,
-                          cast_bytes=cast_bytes(m, k), ev=[]))
+                          cast_bytes=cast_bytes(m, k)))
     torch.cuda.synchronize()
     print(f"[bench] device buffers ready ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)",
           file=sys.stderr, flush=True)
 
-    def run_step(step, record):
+    def cast(c, b):
+        binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=stream)
+
+    def gemm(c, b):
+        binding.fp8_gemm_nt(b["q"], b["s"], b["qb"], b["sb"], b["out"], workspace=c["ws"], stream=stream)
+
+    def run_step(step):
         for c in cases:
             b = c["sets"][step % len(c["sets"])]
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e2 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-            binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=stream)
-            if record:
-                e1.record(stream)
-            binding.fp8_gemm_nt(b["q"], b["s"], b["qb"], b["sb"], b["out"], workspace=c["ws"], stream=stream)
-            if record:
-                e2.record(stream)
-                c["ev"].append((e0, e1, e2))
+            cast(c, b)
+            gemm(c, b)
 
     for s in range(args.warmup):
-        run_step(s, False)
+        run_step(s)
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
+    # ---- the timed region: K whole steps, bracketed by two events ----------
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     start.record(stream)
     for s in range(args.steps):
-        run_step(args.warmup + s, True)
+        run_step(args.warmup + s)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -181,32 +189,55 @@ def main():
     print(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall",
           file=sys.stderr, flush=True)
 
+    # ---- per-kernel launch durations: each kernel launched back to back on
+    # the same stream between two events (markers between single launches
+    # would add their own gaps), rotating the input sets as in the steps -----
+    def launch_mean_ms(fn, c, reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        for r in range(2):
+            fn(c, c["sets"][r % len(c["sets"])])
+        e0.record(stream)
+        for r in range(reps):
+            fn(c, c["sets"][r % len(c["sets"])])
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
     total_flop = sum(c["flop"] for c in cases)
     by_shape = []
     for c in cases:
-        cast_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in c["ev"]]))
-        gemm_ms = float(np.mean([b.elapsed_time(d) for _, b, d in c["ev"]]))
+        reps = max(10, min(200, int(2e4 / max(1.0, c["flop"] / 1e9))))
+        batches = [launch_mean_ms(gemm, c, reps) for _ in range(3)]
+        gemm_ms = float(np.median(batches))
+        cast_ms = launch_mean_ms(cast, c, reps)
+        gemm_all = batches
         c["gemm_ms"], c["cast_ms"] = gemm_ms, cast_ms
+        c["gemm_mean_ms"] = float(np.mean(batches))
         tflops = c["flop"] / (gemm_ms * 1e-3) / 1e12
         gbs = c["bytes"] / (gemm_ms * 1e-3) / 1e9
         bound = "mfma" if c["flop"] / c["bytes"] >= RIDGE else "hbm"
         frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
         by_shape.append(dict(m=c["m"], n=c["n"], k=c["k"], gemm_us=round(gemm_ms * 1e3, 2),
+                             gemm_us_min_max=[round(min(gemm_all) * 1e3, 2), round(max(gemm_all) * 1e3, 2)],
                              cast_us=round(cast_ms * 1e3, 2), tflops=round(tflops, 1), gbs=round(gbs, 1),
                              bound=bound, frac=round(frac, 4),
                              cast_gbs=round(c["cast_bytes"] / (cast_ms * 1e-3) / 1e9, 1)))
     dom = max(cases, key=lambda c: c["gemm_ms"])
     dom_bound = "mfma" if dom["flop"] / dom["bytes"] >= RIDGE else "hbm"
+    # mean launch duration (HIP events on the launch stream), as rocprofv3 averages
     if dom_bound == "mfma":
-        achieved = dom["flop"] / (dom["gemm_ms"] * 1e-3) / 1e12
+        achieved = dom["flop"] / (dom["gemm_mean_ms"] * 1e-3) / 1e12
         roof = dict(bound="mfma", achieved=round(achieved, 1), peak=PEAK_FP8_TFLOPS, unit="TFLOP/s")
     else:
-        achieved = dom["bytes"] / (dom["gemm_ms"] * 1e-3) / 1e9
+        achieved = dom["bytes"] / (dom["gemm_mean_ms"] * 1e-3) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBS, unit="GB/s")
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(dom["m"], dom["n"], dom["k"])
     roof["kernel"] = f"fp8_gemm_nt m={dom['m']} n={dom['n']} k={dom['k']}"
-    roof["per_launch"] = (f"{dom['flop']:.4g} FLOP" if dom_bound == "mfma" else f"{dom['bytes']:.4g} B")
+    roof["per_launch"] = (f"{dom['flop']:.4g} FLOP (2*m*n*k)" if dom_bound == "mfma"
+                          else f"{dom['bytes']:.4g} B (A + B + scales + bf16 out)")
+    roof["mean_launch_us"] = round(dom["gemm_mean_ms"] * 1e3, 2)
 
     small = [c for c in cases if c["m"] <= 256]
     large = [c for c in cases if c["m"] > 256]
@@ -239,33 +270,86 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_rows)
+        result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(shapes, host, rows_per_shape):
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_04_amd", "csrc", f)
+                  for f in ("gemm_kernel.hpp", "device_common.hpp", "fp8gemm.hip")]
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(m, n, k):
+    """HBM bytes per launch of the GEMM for this shape, from the committed
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary (scaled by the copy-kernel
+    calibration recorded with it); None when no summary matches this shape
+    and the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    digest = kernel_source_digest()
+    for line in text.splitlines():
+        if line.startswith("traffic:"):
+            rec = json.loads(line[len("traffic:"):])
+            if rec.get("shape") == [m, n, k] and rec.get("kernel_sources") == digest:
+                return rec["hbm_bytes_per_launch"]
+    return None
+
+
+def copy_calibration(nbytes, steps):
+    """A plain device-to-device copy of nbytes, repeated: the reference that
+    scales the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "launches": steps}), flush=True)
+
+
+def cpu_baseline(shapes, host, target_s):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    the first `rows_per_shape` rows of every shape, cast + GEMM, all host
-    threads.  Scaled to the metric's unit (TFLOP/s of GEMM work)."""
+    the first r rows of every shape (cast + GEMM), all host threads, with r
+    sized from a short calibration so the sample takes about `target_s`
+    seconds.  Scaled to the metric's unit (TFLOP/s of GEMM work)."""
     import oracle
     threads = oracle.hardware_threads()
     wq = {}
     for (m, n, k) in shapes:
         if (n, k) not in wq:
             wq[(n, k)] = oracle.cast_128x128(host[(n, k)], nthreads=threads)  # offline weights: not timed
-    flop = 0.0
-    t = 0.0
-    for (m, n, k) in shapes:
-        r = min(m, rows_per_shape)
-        x = np.ascontiguousarray(host[(m, k)][:r])
-        qb, sb = wq[(n, k)]
-        t0 = time.perf_counter()
-        qa, sa = oracle.cast_1x128(x, nthreads=threads)
-        oracle.gemm_nt(qa, sa, qb, sb, nthreads=threads)
-        t += time.perf_counter() - t0
-        flop += 2.0 * r * n * k
+
+    def run(rows):
+        flop, t = 0.0, 0.0
+        for (m, n, k) in shapes:
+            r = min(m, rows)
+            x = np.ascontiguousarray(host[(m, k)][:r])
+            qb, sb = wq[(n, k)]
+            t0 = time.perf_counter()
+            qa, sa = oracle.cast_1x128(x, nthreads=threads)
+            oracle.gemm_nt(qa, sa, qb, sb, nthreads=threads)
+            t += time.perf_counter() - t0
+            flop += 2.0 * r * n * k
+        return flop, t
+
+    f0, t0 = run(8)
+    rows = int(max(8, min(max(m for m, _, _ in shapes), 8 * target_s / max(t0, 1e-3))))
+    flop, t = run(rows)
     return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows_per_shape} rows (all rows if fewer) of every shape: cast + GEMM, "
+            "sample": f"first {rows} rows (all rows if fewer) of every shape, cast + GEMM: "
                       f"{flop / 2e9:.1f} G MAC in {t:.1f} s"}
 
 

@@ -87,6 +87,34 @@ __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voffse
                :: "s"(lds_wave_base), "v"(voffset), "s"(sbase) : "memory");
 }
 
+// Same path with 4 bytes per lane (global_load_lds_dword): lane i's dword
+// lands at LDS address lds_wave_base + 4 * i.
+__device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voffset, uint32_t lds_wave_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds_wave_base), "v"(voffset), "s"(sbase) : "memory");
+}
+
+// Device-coherent 16-byte global store / load (sc1: past the per-XCD L2s, so
+// another XCD sees the data once the access has completed).  Used for split-K
+// partial sums that another workgroup, possibly on another XCD, adds up.
+// The load waits for its own data.
+__device__ __forceinline__ void store16_coherent(float* p, const v4f& v) {
+  asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(p), "v"(v) : "memory");
+}
+// Issue only: the data may be used after wait_coherent() has returned it.
+__device__ __forceinline__ v4f load16_coherent_issue(const float* p) {
+  v4f v;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+// Waits for every outstanding vector-memory access; the values pass through
+// the statement, so no use of them can be scheduled before the wait.
+__device__ __forceinline__ void wait_coherent(v4f (&t)[8]) {
+  asm volatile("s_waitcnt vmcnt(0)"
+               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7])
+               :: "memory");
+}
+
 // Uniform (per-wave) value: keeps address arithmetic in scalar registers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 

@@ -75,46 +75,84 @@ int check_ld(int64_t ld, int64_t rows) {
 }
 
 // ---- dense configuration ---------------------------------------------------
-// Kernel shapes (BM tokens x BN outputs per workgroup, wave grid, LDS stages):
-//   kDenseM64   64 x 128, waves 1x4, 4 stages  (m <= 64)
-//   kDenseM128 128 x 128, waves 2x2, 3 stages  (m <= 128)
-//   kDenseBig  256 x 256, waves 4x2 (two per SIMD), 2 stages  (m > 128)
+// Kernel shapes: BM tokens x BN outputs per workgroup, wave grid, LDS stages.
 // A wave's accumulator tile is at most 128 x 64 (128 VGPRs): the promotion
-// FMAs need their accumulators in architectural VGPRs, and two waves per SIMD
-// (eight per workgroup) share the SIMD's registers so that one wave's LDS
-// and barrier waits are covered by the other's MFMAs.
-// When the tile count would leave CUs idle, K is split across workgroups and
-// the partials are summed in a fixed order.
-enum DenseKind { kDenseM64 = 0, kDenseM128 = 1, kDenseBig = 2 };
+// FMAs need their accumulators in architectural VGPRs.  The large-M shape
+// runs two waves per SIMD (eight per workgroup) so that one wave's LDS and
+// barrier waits are covered by the other's MFMAs.  Small-M shapes are
+// HBM-bound: narrow N tiles and deep rings keep many copies in flight, and
+// when the tile count would leave CUs idle, K is split across workgroups; the
+// last workgroup to finish a tile adds the partial sums in split order.
+struct KernelShape {
+  int bm, bn, stages, waves;
+};
+enum DenseKind { kS64N64 = 0, kS64N128 = 1, kS128N64 = 2, kS128N128 = 3, kBig = 4, kMid = 5, kS64N32 = 6,
+                 kS128N32 = 7, kKinds = 8 };
+constexpr KernelShape kShapes[kKinds] = {
+    {64, 64, 4, 4},    // m <= 64
+    {64, 128, 4, 4},
+    {128, 64, 4, 4},   // 64 < m <= 128
+    {128, 128, 3, 4},
+    {256, 256, 2, 8},  // m > 128
+    {256, 128, 3, 4},
+    {64, 32, 4, 4},
+    {128, 32, 4, 4},
+};
+constexpr int kMaxSplits = 8;  // the split-K fix-up adds at most this many partials
 
 struct DenseConfig {
-  int kind, bm, bn, tiles_m, tiles_n, splits, gps;
+  int kind, tiles_m, tiles_n, splits, gps;
 };
+
+int env_int(const char* name, int fallback) {
+  const char* v = std::getenv(name);
+  return (v && *v) ? std::atoi(v) : fallback;
+}
 
 DenseConfig dense_config(int m, int n, int k, bool allow_split) {
   DenseConfig c{};
-  if (m <= 64) { c.kind = kDenseM64; c.bm = 64; c.bn = 128; }
-  else if (m <= 128) { c.kind = kDenseM128; c.bm = 128; c.bn = 128; }
-  else { c.kind = kDenseBig; c.bm = 256; c.bn = 256; }
-  c.tiles_m = int(cdiv(m, c.bm));
-  c.tiles_n = int(cdiv(n, c.bn));
+  c.kind = m <= 64 ? kS64N32 : (m <= 128 ? kS128N32 : kBig);
+  const int cus0 = effective_cus();
+  // large M but few 256 x 256 tiles: narrower tiles with split-K fill the CUs
+  if (c.kind == kBig && cdiv(m, 256) * cdiv(n, 256) < cus0 / 2) c.kind = kS128N64;
+  const int forced = env_int("FP8G_FORCE_CONFIG", -1);  // debugging and tuning only
+  if (forced >= 0 && forced < kKinds) c.kind = forced;
+  const KernelShape& ks = kShapes[c.kind];
+  c.tiles_m = int(cdiv(m, ks.bm));
+  c.tiles_n = int(cdiv(n, ks.bn));
   const int kg = k / 128;
   c.splits = 1;
   c.gps = kg;
   const int64_t tiles = int64_t(c.tiles_m) * c.tiles_n;
   const int cus = effective_cus();
-  if (allow_split && tiles < cus) {
-    int s = int(std::min<int64_t>(kg, cdiv(cus, tiles)));
-    const char* force = std::getenv("FP8G_SPLITS");
-    if (force) s = std::max(1, std::min(kg, std::atoi(force)));
+  const bool can_split = ks.bm * (ks.bn + 4) * 4 <= ks.stages * (ks.bm + ks.bn) * 128;  // staged tile fits the ring
+  // Split only when it at least doubles the workgroup count: each split
+  // adds a partial-sum round trip through memory at the end of the kernel.
+  if (allow_split && can_split && 2 * tiles <= cus + tiles / 2) {
+    int s = int(std::min<int64_t>(kg, (cus + tiles / 2) / tiles));
+    s = std::max(1, std::min(std::min(kg, kMaxSplits), env_int("FP8G_SPLITS", s)));
     c.gps = int(cdiv(kg, s));
     c.splits = int(cdiv(kg, c.gps));
   }
   return c;
 }
 
+// Workspace of a split configuration: one 8-byte arrival counter per output
+// tile (rounded up to 256 bytes), then [splits][m][n] fp32 partial sums.
+size_t counter_bytes(const DenseConfig& c) {
+  return size_t(cdiv(int64_t(c.tiles_m) * c.tiles_n * 8, 256)) * 256;
+}
+
 size_t dense_workspace(const DenseConfig& c, int m, int n) {
-  return c.splits > 1 ? size_t(c.splits) * size_t(m) * size_t(n) * sizeof(float) : 0;
+  return c.splits > 1 ? counter_bytes(c) + size_t(c.splits) * size_t(m) * size_t(n) * sizeof(float) : 0;
+}
+
+// Per-call tag of the split-K arrival counters (never 0).
+std::atomic<unsigned> g_epoch{0};
+unsigned next_epoch() {
+  unsigned e = g_epoch.fetch_add(1) + 1;
+  if (e == 0) e = g_epoch.fetch_add(1) + 1;
+  return e;
 }
 
 template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT>
@@ -126,9 +164,18 @@ void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
 template <bool SPLIT>
 void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
   switch (kind) {
-    case kDenseM64: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
-    case kDenseM128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
-    default: launch_gemm<256, 256, 4, 2, 2, kDense, SPLIT>(p, grid, s); break;
+    case kS64N64: launch_gemm<64, 64, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
+    case kS64N128: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
+    case kS128N64: launch_gemm<128, 64, 2, 2, 4, kDense, SPLIT>(p, grid, s); break;
+    case kS128N128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
+    case kMid: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
+    case kS64N32: launch_gemm<64, 32, 2, 2, 4, kDense, SPLIT>(p, grid, s); break;
+    case kS128N32: launch_gemm<128, 32, 4, 1, 4, kDense, SPLIT>(p, grid, s); break;
+    default:
+      // the 256 x 256 tile cannot stage a split partial (dense_config never
+      // asks for it)
+      if constexpr (!SPLIT) launch_gemm<256, 256, 4, 2, 2, kDense, false>(p, grid, s);
+      break;
   }
 }
 
@@ -178,7 +225,11 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
 
   GemmParams p{};
   p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
-  p.partial = static_cast<float*>(workspace);
+  if (c.splits > 1) {
+    p.tile_counters = static_cast<unsigned long long*>(workspace);
+    p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c));
+    p.epoch = next_epoch();
+  }
   p.sa_ld = lhs_scales_ld;
   p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
   p.tiles_m = c.tiles_m; p.tiles_n = c.tiles_n; p.splits = c.splits; p.groups_per_split = c.gps;
@@ -189,11 +240,7 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
                  c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
   if (c.splits > 1) {
     launch_dense<true>(c.kind, p, grid, s);
-    if (int st = launched("gemm")) return st;
-    const int64_t mn = int64_t(m) * n;
-    hipLaunchKernelGGL(fp8g::splitk_reduce_kernel, dim3(unsigned(cdiv(mn / 4, 256))), dim3(256), 0, s,
-                       static_cast<const float*>(workspace), out, mn, c.splits);
-    return launched("split-K reduce");
+    return launched("gemm");
   }
   launch_dense<false>(c.kind, p, grid, s);
   return launched("gemm");

@@ -39,6 +39,8 @@ struct GemmParams {
   const float* sb;           // RHS scales [G][NB][KG]
   uint16_t* out;             // BF16 output
   float* partial;            // split-K partial sums [splits][m][n] (dense only)
+  unsigned long long* tile_counters;  // split-K arrival counters, one per output tile
+  unsigned int epoch;        // this call's tag for the arrival counters (never 0)
   const int32_t* m_indices;  // contiguous: group of each row
   const int32_t* masked_m;   // masked: valid rows per group
   int64_t sa_ld;
@@ -269,14 +271,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
     for (int j = 0; j < TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int wrow_m = wm * WM, wrow_n = wn * WN;
-  // The tile's RHS scale rows go to LDS once, so the K loop reads them
-  // without a global load.
-#pragma unroll
-  for (int b = 0; b < SB_BLOCKS; ++b) {
-    const int blk = min(n0 / 128 + b, p.nb - 1);
-    for (int g = threadIdx.x; g < p.kg; g += blockDim.x) sb_cache[b][g] = SB[int64_t(blk) * p.kg + g];
+  // The tile's RHS scale rows (this split's K groups) go to LDS once, by the
+  // same direct copy and ahead of the operand copies, so the first ring wait
+  // also covers them and the K loop reads them without a global load.
+  {
+    const uint32_t sb_lds = uniform(int(lds_addr(&sb_cache[0][0])));
+    for (int c = wave; c < SB_BLOCKS * ((niter + 63) / 64); c += NW) {
+      const int b = c % SB_BLOCKS, part = c / SB_BLOCKS;
+      const int blk = min(n0 / 128 + b, p.nb - 1);
+      const int g = min(g_begin + 64 * part + lane, g_end - 1);
+      copy4_to_lds(SB + int64_t(blk) * p.kg, 4u * uint32_t(g), sb_lds + 4 * (b * kMaxGroups + 64 * part));
+    }
   }
-  const float* sb_row = sb_cache[wrow_n / 128] + g_begin;
+  const float* sb_row = sb_cache[wrow_n / 128];
   // In the masked layout a wave whose tokens are all past the count skips
   // the products (its copies still run: the ring is shared).
   const bool wave_live = MODE != kMasked || m0 + wrow_m < rows;
@@ -291,7 +298,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   f.b1 = smem + B_REGION + wrow_n * kRowBytes + tile_byte(lr, c0 + 1);
   f.s = reinterpret_cast<const float*>(smem + S_REGION) + wrow_m + lr;
 
-  if (0 < niter) issue(Int<0>{}, g_begin);
+  if (0 < niter) issue(Int<0>{}, g_begin);  // (the scale-row copies above are older)
   if constexpr (STAGES > 2) if (1 < niter) issue(Int<1>{}, g_begin + 1);
   if constexpr (STAGES > 3) if (2 < niter) issue(Int<2>{}, g_begin + 2);
 
@@ -312,17 +319,82 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   }
 
   // ---- epilogue: lane holds n = col..col+3 of one token per sub-tile -------
+  if constexpr (SPLIT) {
+    // Publish this split's partial tile, then count arrivals on the tile.
+    // The last workgroup to arrive adds all partials in split order
+    // (p_0 + p_1 + ... + p_{S-1}), so the result does not depend on arrival
+    // order.  The tile is staged through LDS (free once the K loop is done)
+    // so that partials move as whole rows of 16-byte device-coherent
+    // accesses, which go past the per-XCD L2s: retiring the stores before
+    // the arrival is counted makes them visible to the last workgroup
+    // without any cache-wide write-back or invalidate.
+    static_assert(BM * (BN + 4) * 4 <= RING, "staged partial tile fits in the ring");
+    constexpr int LDT = BN + 4;  // padded row stride (floats) of the staged tile
+    constexpr int CHUNKS = BM * BN / 4;
+    float* stage = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done with the ring
 #pragma unroll
-  for (int i = 0; i < TN; ++i) {
-    const int col = n0 + wrow_n + 16 * i + 4 * (lane >> 4);
+    for (int i = 0; i < TN; ++i)
 #pragma unroll
-    for (int j = 0; j < TM; ++j) {
-      const int tok = m0 + wrow_m + 16 * j + (lane & 15);
-      if (tok < rows && col < p.n) {
-        if constexpr (SPLIT) {
-          float* P = p.partial + (int64_t(split) * p.m + tok) * p.n + col;
-          *reinterpret_cast<v4f*>(P) = acc[i][j];
-        } else {
+      for (int j = 0; j < TM; ++j)
+        *reinterpret_cast<v4f*>(stage + (wrow_m + 16 * j + (lane & 15)) * LDT + wrow_n + 16 * i + 4 * (lane >> 4)) =
+            acc[i][j];
+    __syncthreads();
+    const int64_t mn = int64_t(p.m) * p.n;
+    for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
+      const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
+      if (m0 + r < rows && n0 + c4 < p.n)
+        store16_coherent(p.partial + split * mn + int64_t(m0 + r) * p.n + n0 + c4,
+                         *reinterpret_cast<const v4f*>(stage + r * LDT + c4));
+    }
+    __shared__ int last_arrival;
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      // counter word: epoch in the high 32 bits, arrivals in the low 32; a
+      // word from another call (or uninitialised memory) restarts the count
+      unsigned long long* ctr = p.tile_counters + (int64_t(m_tile) * p.tiles_n + n_tile);
+      unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long nxt;
+      do {
+        nxt = (unsigned(old >> 32) == p.epoch) ? old + 1 : ((unsigned long long)p.epoch << 32) | 1ull;
+      } while (!__hip_atomic_compare_exchange_strong(ctr, &old, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+      const bool last = unsigned(nxt) == unsigned(p.splits);
+      if (last) __hip_atomic_store(ctr, (unsigned long long)p.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_arrival = last;
+    }
+    __syncthreads();
+    if (!last_arrival) return;
+    // all splits of a chunk are requested before one wait (kMaxSplits <= 8)
+    for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
+      const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
+      if (m0 + r < rows && n0 + c4 < p.n) {
+        const float* P = p.partial + int64_t(m0 + r) * p.n + n0 + c4;
+        const v4f mine = *reinterpret_cast<const v4f*>(stage + r * LDT + c4);
+        v4f t[8];
+#pragma unroll
+        for (int sp = 0; sp < 8; ++sp)
+          t[sp] = (sp < p.splits && sp != split) ? load16_coherent_issue(P + sp * mn) : mine;
+        wait_coherent(t);
+        v4f sum = t[0];
+#pragma unroll
+        for (int sp = 1; sp < 8; ++sp)
+          if (sp < p.splits) sum += t[sp];
+        uint2 v;
+        v.x = pack_bf16x2(sum[0], sum[1]);
+        v.y = pack_bf16x2(sum[2], sum[3]);
+        *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * p.n + n0 + c4) = v;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < TN; ++i) {
+      const int col = n0 + wrow_n + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+      for (int j = 0; j < TM; ++j) {
+        const int tok = m0 + wrow_m + 16 * j + (lane & 15);
+        if (tok < rows && col < p.n) {
           uint2 v;
           v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
           v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
@@ -331,20 +403,6 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
       }
     }
   }
-}
-
-// Fixed-order sum of split-K partials: out = bf16(p_0 + p_1 + ... + p_{S-1}),
-// four outputs per thread.
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* partial, uint16_t* out,
-                                                             int64_t mn, int splits) {
-  const int64_t i = (int64_t(blockIdx.x) * 256 + threadIdx.x) * 4;
-  if (i >= mn) return;
-  v4f s = *reinterpret_cast<const v4f*>(partial + i);
-  for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const v4f*>(partial + int64_t(sp) * mn + i);
-  uint2 v;
-  v.x = pack_bf16x2(s[0], s[1]);
-  v.y = pack_bf16x2(s[2], s[3]);
-  *reinterpret_cast<uint2*>(out + i) = v;
 }
 
 }  // namespace fp8g

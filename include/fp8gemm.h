@@ -63,12 +63,18 @@ enum { FP8G_F32 = 0, FP8G_BF16 = 1 };
  *   lhs        [m][k] E4M3 codes;   lhs_scales [KG][lhs_scales_ld] FP32
  *   rhs        [n][k] E4M3 codes;   rhs_scales [NB][KG] FP32
  *   out        [m][n] BF16 (written in full)
- *   workspace  optional device scratch for split-K partial sums; pass the
- *              size reported by fp8_gemm_workspace_bytes() to allow split-K.
- *              A smaller (or NULL) workspace selects a configuration without
- *              split-K; it is never an error.  The result does not depend on
- *              whether split-K is used up to FP32 rounding order, and a given
- *              configuration always produces bit-identical output. */
+ *   workspace  optional device scratch (16-byte aligned) for split-K: per
+ *              output tile an arrival counter, then the FP32 partial sums.
+ *              Pass at least fp8_gemm_workspace_bytes() bytes to allow
+ *              split-K; a smaller (or NULL) workspace selects a configuration
+ *              without split-K, which is never an error.  The workspace needs
+ *              no initialisation (the counters are tagged per call) and is
+ *              left in a state the next call accepts, also under HIP graph
+ *              replay; two calls that may run concurrently must not share a
+ *              workspace.  The last workgroup to finish a tile adds the
+ *              partials in split order, so a given configuration always
+ *              produces bit-identical output; results with and without
+ *              split-K differ only by FP32 rounding order. */
 int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
                 const uint8_t* rhs, const float* rhs_scales,
                 uint16_t* out, int m, int n, int k,

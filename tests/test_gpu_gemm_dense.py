@@ -149,3 +149,62 @@ def test_dense_zero_rows_is_a_noop():
     out = torch.empty((0, 8), dtype=torch.bfloat16, device="cuda")
     binding.fp8_gemm_nt(lhs, sa, rhs, sb, out)
     torch.cuda.synchronize()
+
+
+def _dense_dev(qa, sa, qb, sb):
+    from _gpu import sa_mn_major
+    return dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb)
+
+
+@pytest.mark.parametrize("m,n,k", [(64, 1024, 4096), (128, 512, 7168)])
+def test_splitk_workspace_needs_no_initialisation(m, n, k):
+    """The split-K arrival counters are tagged per call: a workspace full of
+    random bytes gives the same bits as a zeroed one, call after call."""
+    require_gpu()
+    qa, sa, qb, sb = dense_case(m, n, k, seed=11)
+    a, s_, b, t = _dense_dev(qa, sa, qb, sb)
+    nbytes = binding.fp8_gemm_workspace_bytes(m, n, k)
+    assert nbytes > 0, "shape expected to use split-K"
+    ws0 = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    junk = np.random.default_rng(3).integers(0, 256, nbytes, dtype=np.uint8)
+    ws1 = dev(junk).view(torch.float32)
+    outs = []
+    for ws in (ws0, ws1, ws1, ws0):
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        binding.fp8_gemm_nt(a, s_, b, t, out, workspace=ws)
+        outs.append(out.view(torch.int16).cpu().numpy().view(np.uint16))
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    assert_close(outs[0], oracle.gemm_nt(qa, sa, qb, sb), "split-K")
+
+
+def test_splitk_graph_replay_matches_eager():
+    """A captured split-K call, replayed several times with eager work in
+    between, reproduces the eager result bit for bit each time."""
+    require_gpu()
+    m, n, k = 64, 2048, 7168
+    qa, sa, qb, sb = dense_case(m, n, k, seed=12)
+    a, s_, b, t = _dense_dev(qa, sa, qb, sb)
+    ws = torch.zeros(binding.fp8_gemm_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device="cuda")
+    eager = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    binding.fp8_gemm_nt(a, s_, b, t, eager, workspace=ws)
+    torch.cuda.synchronize()
+    ref = eager.view(torch.int16).cpu().numpy()
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.fp8_gemm_nt(a, s_, b, t, out, workspace=ws)  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        binding.fp8_gemm_nt(a, s_, b, t, out, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref), f"replay {rep}"
+        # eager work between replays (also moves the counters' epoch on)
+        binding.fp8_gemm_nt(a, s_, b, t, eager, workspace=ws)
+        torch.cuda.synchronize()

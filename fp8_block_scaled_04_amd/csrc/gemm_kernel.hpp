@@ -32,6 +32,9 @@ namespace fp8g {
 
 enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
 
+constexpr int kXcds = 8;    // XCDs of an MI355X; workgroups are dealt to them round-robin
+constexpr int kGroupM = 4;  // M-tiles walked together in the dense tile order
+
 struct GemmParams {
   const uint8_t* a;          // LHS codes
   const float* sa;           // LHS scales, MN-major [KG][sa_ld] (per group for masked)
@@ -198,11 +201,30 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   // ---- work unit ------------------------------------------------------
   int bid = blockIdx.x;
   int split = 0;
-  if constexpr (SPLIT) { split = bid % p.splits; bid /= p.splits; }
-  const int n_tile = bid % p.tiles_n;
-  bid /= p.tiles_n;
-  const int m_tile = bid % p.tiles_m;
-  const int group = bid / p.tiles_m;  // masked only
+  int n_tile, m_tile, group = 0;
+  if constexpr (MODE == kDense) {
+    // Workgroups are dispatched to the 8 XCDs round-robin and each XCD has
+    // its own L2: give XCD x a contiguous range of logical tiles, walked in
+    // groups of kGroupM M-tiles (M fastest), so the tiles an XCD runs at
+    // once share a few A and B K-slices.  (A bijection, so correctness does
+    // not depend on the dispatch order.)
+    const int total = gridDim.x;
+    const int xcd = bid % kXcds, slot = bid / kXcds;
+    const int per = total / kXcds, extra = total % kXcds;
+    int L = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
+    if constexpr (SPLIT) { split = L % p.splits; L /= p.splits; }
+    const int band = kGroupM * p.tiles_n;
+    const int first_m = (L / band) * kGroupM;
+    const int rows_in_band = min(p.tiles_m - first_m, kGroupM);
+    const int in_band = L % band;
+    m_tile = first_m + in_band % rows_in_band;
+    n_tile = in_band / rows_in_band;
+  } else {
+    n_tile = bid % p.tiles_n;
+    bid /= p.tiles_n;
+    m_tile = bid % p.tiles_m;
+    group = bid / p.tiles_m;  // masked only
+  }
   const int m0 = m_tile * BM, n0 = n_tile * BN;
 
   const uint8_t* A = p.a;

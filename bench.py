@@ -13,8 +13,9 @@ two uses of the same copy (4x the 256 MB Infinity Cache).
 
 Prints one JSON line.  `value` is the sweep's total GEMM FLOP divided by the
 measured step time (cast included; the steps are bracketed by two events
-only).  Per-kernel durations come from a second phase that launches each
-kernel back to back between two events on the same stream.  `roofline`
+only).  Per-kernel durations come from a second phase that captures many
+launches of one kernel into a HIP graph and times its replays between two
+events on the same stream.  `roofline`
 describes the kernel that takes the most time: algorithmic FLOP (or bytes)
 per launch divided by its mean launch duration.  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
@@ -82,6 +83,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--digest", action="store_true", help="print the GEMM kernel source digest and exit")
+    ap.add_argument("--no-grouped", action="store_true",
+                    help="skip the grouped-GEMM measurements (MoE prefill and decode configurations)")
     args = ap.parse_args()
     if args.digest:
         print(kernel_source_digest())
@@ -156,11 +159,11 @@ def main():
     print(f"[bench] device buffers ready ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)",
           file=sys.stderr, flush=True)
 
-    def cast(c, b):
-        binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=stream)
+    def cast(c, b, st=stream):
+        binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=st)
 
-    def gemm(c, b):
-        binding.fp8_gemm_nt(b["q"], b["s"], b["qb"], b["sb"], b["out"], workspace=c["ws"], stream=stream)
+    def gemm(c, b, st=stream):
+        binding.fp8_gemm_nt(b["q"], b["s"], b["qb"], b["sb"], b["out"], workspace=c["ws"], stream=st)
 
     def run_step(step):
         for c in cases:
@@ -189,28 +192,14 @@ def main():
     print(f"[bench] timed {args.steps} steps: {total_ms:.2f} ms on the GPU clock, {wall * 1e3:.2f} ms wall",
           file=sys.stderr, flush=True)
 
-    # ---- per-kernel launch durations: each kernel launched back to back on
-    # the same stream between two events (markers between single launches
-    # would add their own gaps), rotating the input sets as in the steps -----
-    def launch_mean_ms(fn, c, reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        for r in range(2):
-            fn(c, c["sets"][r % len(c["sets"])])
-        e0.record(stream)
-        for r in range(reps):
-            fn(c, c["sets"][r % len(c["sets"])])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / reps
-
+    # ---- per-kernel launch durations -------------------------------------
     total_flop = sum(c["flop"] for c in cases)
     by_shape = []
     for c in cases:
         reps = max(10, min(200, int(2e4 / max(1.0, c["flop"] / 1e9))))
-        batches = [launch_mean_ms(gemm, c, reps) for _ in range(3)]
+        batches = replay_mean_ms(torch, stream, lambda b, st: gemm(c, b, st), c["sets"], reps, 3)
         gemm_ms = float(np.median(batches))
-        cast_ms = launch_mean_ms(cast, c, reps)
+        cast_ms = float(np.median(replay_mean_ms(torch, stream, lambda b, st: cast(c, b, st), c["sets"], reps, 1)))
         gemm_all = batches
         c["gemm_ms"], c["cast_ms"] = gemm_ms, cast_ms
         c["gemm_mean_ms"] = float(np.mean(batches))
@@ -269,9 +258,170 @@ def main():
         "by_shape": by_shape,
     }
 
+    if not args.no_grouped and not args.shape:
+        del cases, sets
+        torch.cuda.empty_cache()
+        result["grouped"] = grouped_measurements(stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+GROUPED = {
+    "contiguous": dict(groups=8, n=4096, k=7168),
+    "masked": dict(groups=16, max_m=256, n=4096, k=7168),
+}
+
+
+def replay_mean_ms(torch, stream, fn, sets, reps, batches):
+    """Mean duration of one launch: `reps` launches of fn (rotating the input
+    sets) are captured into one HIP graph, which is replayed `batches` times
+    on `stream` between two events each.  Replaying a graph issues the
+    kernels back to back on the GPU, so kernels shorter than the host's
+    per-call launch cost are timed by the GPU, not by the host."""
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for r in range(2):
+            fn(sets[r % len(sets)], None)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(reps):
+            fn(sets[r % len(sets)], None)
+    graph.replay()
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(batches):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        graph.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / reps)
+    del graph
+    return out
+
+
+def grouped_measurements(stream):
+    """The two grouped GEMMs at their MoE shapes, timed like the dense shapes
+    (launches back to back between two events, rotated input sets):
+      contiguous (prefill): G=8 experts, n=4096, k=7168, expert rows 128*U{4..32}
+        concatenated in expert order, m_indices per row;
+      masked (decode): G=16 slots of max_m=256 rows, n=4096, k=7168, valid rows
+        per group U{0..256} in a device tensor.
+    Seeded N(0,1) activations and weights, quantised on the GPU (1x128 and
+    128x128 casts).  FLOP and bytes count valid rows only."""
+    import torch
+    from fp8_block_scaled_04_amd import binding, synth
+    out = []
+
+    def timed(fn, sets, reps):
+        batches = replay_mean_ms(torch, stream, fn, sets, reps, 3)
+        return float(np.median(batches)), float(np.mean(batches)), batches
+
+    def weights(G, n, k):
+        kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+        w = synth.normal_f32(0, synth.S_RHS, (G, n, k))
+        qb = torch.empty((G, n, k), dtype=torch.uint8, device="cuda")
+        sb = torch.empty((G, nb, kg), dtype=torch.float32, device="cuda")
+        for g in range(G):
+            wd = torch.from_numpy(w[g]).cuda()
+            binding.fp8_cast_per_block(wd, qb[g], sb[g])
+        del w
+        return qb, sb
+
+    def record(name, desc, flop, nbytes, med, mean, batches, extra):
+        tflops = flop / (med * 1e-3) / 1e12
+        gbs = nbytes / (med * 1e-3) / 1e9
+        bound = "mfma" if flop / nbytes >= RIDGE else "hbm"
+        frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
+        rec = dict(kernel=name, workload=desc, gemm_us=round(med * 1e3, 2), mean_launch_us=round(mean * 1e3, 2),
+                   gemm_us_min_max=[round(min(batches) * 1e3, 2), round(max(batches) * 1e3, 2)],
+                   tflops=round(tflops, 1), gbs=round(gbs, 1), bound=bound, frac=round(frac, 4),
+                   flop=flop, alg_bytes=nbytes)
+        rec.update(extra)
+        out.append(rec)
+        print(f"[bench] {name}: {med * 1e3:.1f} us, {tflops:.0f} TFLOP/s, {gbs:.0f} GB/s", file=sys.stderr,
+              flush=True)
+
+    # ---- contiguous layout ---------------------------------------------------
+    c = GROUPED["contiguous"]
+    G, n, k = c["groups"], c["n"], c["k"]
+    kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+    sizes = synth.contiguous_group_sizes(G, 0)
+    M = int(sizes.sum())
+    x = synth.normal_f32(0, synth.S_LHS, (M, k))
+    m_idx = np.repeat(np.arange(G, dtype=np.int32), sizes)
+    xd = torch.from_numpy(x).cuda()
+    del x
+    qa = torch.empty((M, k), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((kg, M), dtype=torch.float32, device="cuda")
+    binding.fp8_cast_per_token_group(xd, qa, sa)
+    del xd
+    qb, sb = weights(G, n, k)
+    mi = torch.from_numpy(m_idx).cuda()
+    foot = M * k + G * n * k + M * n * 2
+    nsets = max(1, math.ceil(ROTATE_BYTES / foot))
+    sets = [(qa, sa, qb, sb, torch.empty((M, n), dtype=torch.bfloat16, device="cuda"))]
+    for _ in range(1, nsets):
+        sets.append((qa.clone(), sa.clone(), qb.clone(), sb.clone(),
+                     torch.empty((M, n), dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+
+    def run_c(bufs, st):
+        a, s_, b, t, o = bufs
+        binding.fp8_grouped_gemm_contiguous(a, s_, b, t, o, mi, stream=st)
+
+    med, mean, batches = timed(run_c, sets, 20)
+    flop = 2.0 * M * n * k
+    nbytes = M * k + G * n * k + M * kg * 4 + G * nb * kg * 4 + M * n * 2 + M * 4
+    record("fp8_grouped_gemm_contiguous",
+           f"MoE prefill: G={G} experts, n={n}, k={k}, rows per expert 128*U{{4..32}} (seed 0), M={M}",
+           flop, nbytes, med, mean, batches, dict(m_total=M, group_rows=[int(v) for v in sizes], rotated_sets=nsets))
+    del sets, qa, sa, qb, sb, mi
+    torch.cuda.empty_cache()
+
+    # ---- masked layout ---------------------------------------------------------
+    c = GROUPED["masked"]
+    G, max_m, n, k = c["groups"], c["max_m"], c["n"], c["k"]
+    kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+    counts = synth.masked_counts(G, max_m, 0)
+    x = synth.normal_f32(0, synth.S_LHS, (G, max_m, k))
+    qa = torch.empty((G, max_m, k), dtype=torch.uint8, device="cuda")
+    sa = torch.empty((G, kg, max_m), dtype=torch.float32, device="cuda")
+    for g in range(G):
+        binding.fp8_cast_per_token_group(torch.from_numpy(x[g]).cuda(), qa[g], sa[g])
+    del x
+    qb, sb = weights(G, n, k)
+    mm = torch.from_numpy(counts).cuda()
+    foot = G * max_m * k + G * n * k + G * max_m * n * 2
+    nsets = max(1, math.ceil(ROTATE_BYTES / foot))
+    sets = [(qa, sa, qb, sb, torch.empty((G, max_m, n), dtype=torch.bfloat16, device="cuda"))]
+    for _ in range(1, nsets):
+        sets.append((qa.clone(), sa.clone(), qb.clone(), sb.clone(),
+                     torch.empty((G, max_m, n), dtype=torch.bfloat16, device="cuda")))
+    torch.cuda.synchronize()
+
+    def run_m(bufs, st):
+        a, s_, b, t, o = bufs
+        binding.fp8_grouped_gemm_masked(a, s_, b, t, o, mm, stream=st)
+
+    med, mean, batches = timed(run_m, sets, 20)
+    valid = int(counts.sum())
+    active = int((counts > 0).sum())
+    flop = 2.0 * valid * n * k
+    nbytes = valid * k + active * n * k + valid * kg * 4 + active * nb * kg * 4 + valid * n * 2 + G * 4
+    record("fp8_grouped_gemm_masked",
+           f"MoE decode: G={G} slots of max_m={max_m} rows, n={n}, k={k}, valid rows per group U{{0..{max_m}}} "
+           f"(seed 0), {valid} valid rows",
+           flop, nbytes, med, mean, batches, dict(valid_rows=valid, masked_m=[int(v) for v in counts],
+                                                  rotated_sets=nsets))
+    del sets, qa, sa, qb, sb, mm
+    torch.cuda.empty_cache()
+    return out
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")

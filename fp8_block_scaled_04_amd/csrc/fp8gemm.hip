@@ -266,12 +266,15 @@ int fp8_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int
   p.m_indices = m_indices;
   p.sa_ld = lhs_scales_ld;
   p.m = m_total; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
+  // Tiles are one or two 128-row blocks of one group (the kernel finds them
+  // from m_indices); there are at most as many tiles as blocks.
   p.tiles_m = m_total / 128; p.tiles_n = int(cdiv(n, 256)); p.splits = 1; p.groups_per_split = p.kg;
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n;
+  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
   if (log_enabled())
-    std::fprintf(stderr, "[fp8gemm] contiguous M=%d n=%d k=%d G=%d grid=%lld\n", m_total, n, k, num_groups,
+    std::fprintf(stderr, "[fp8gemm] contiguous M=%d n=%d k=%d G=%d grid<=%lld\n", m_total, n, k, num_groups,
                  (long long)grid);
-  launch_gemm<128, 256, 1, 4, 3, kContiguous, false>(p, grid, static_cast<hipStream_t>(stream));
+  launch_gemm<256, 256, 4, 2, 2, kContiguous, false>(p, grid, static_cast<hipStream_t>(stream));
   return launched("contiguous gemm");
 }
 

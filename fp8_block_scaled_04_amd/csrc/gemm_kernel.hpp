@@ -171,6 +171,88 @@ __device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs
 template <int N>
 struct Int { static constexpr int value = N; };
 
+// Tiles of the contiguous layout.  Each aligned 128-row block b carries one
+// group index, m_indices[128 b].  A maximal run of blocks with the same
+// non-negative index is cut into tiles of two blocks from its first block on
+// (the last tile of an odd run has one block), so a 256-row tile never mixes
+// two groups and no tile is spent on a group boundary.  Blocks with a
+// negative index belong to no tile.  The host cannot know the tile count,
+// so every wave derives it from the (L2-resident) index array by a
+// wave-wide scan: lane j walks blocks [lo, hi), the j-th chunk of the
+// blocks.
+struct ContigScan {
+  int tiles;  // tiles in total (the same in every lane)
+  int lo, hi;
+  int in_rs;  // first block of the run in effect just before lo
+  int base;   // tiles that start in the chunks of lanes < j
+  int count;  // tiles that start in this lane's chunk
+};
+
+__device__ __forceinline__ int block_group(const int32_t* idx, int b) { return idx[int64_t(b) * 128]; }
+
+__device__ __forceinline__ ContigScan contiguous_scan(const int32_t* idx, int nblk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int chunk = (nblk + kWave - 1) / kWave;
+  ContigScan s;
+  s.lo = min(lane * chunk, nblk);
+  s.hi = min(s.lo + chunk, nblk);
+  int last_rs = -1, prev = s.lo > 0 ? block_group(idx, s.lo - 1) : 0;
+  for (int b = s.lo; b < s.hi; ++b) {
+    const int e = block_group(idx, b);
+    if (b == 0 || e != prev) last_rs = b;
+    prev = e;
+  }
+  int v = last_rs;  // inclusive max-scan over lanes
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(v, d, kWave);
+    if (lane >= d) v = max(v, t);
+  }
+  const int excl = __shfl_up(v, 1, kWave);
+  s.in_rs = lane == 0 ? -1 : excl;
+  int cur = s.in_rs, cnt = 0;
+  prev = s.lo > 0 ? block_group(idx, s.lo - 1) : 0;
+  for (int b = s.lo; b < s.hi; ++b) {
+    const int e = block_group(idx, b);
+    if (b == 0 || e != prev) cur = b;
+    prev = e;
+    if (e >= 0 && ((b - cur) & 1) == 0) ++cnt;
+  }
+  s.count = cnt;
+  int incl = cnt;  // inclusive sum-scan over lanes
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int t = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += t;
+  }
+  s.base = incl - cnt;
+  s.tiles = uniform(__shfl(incl, kWave - 1, kWave));
+  return s;
+}
+
+// First block, block count (1 or 2) and group of tile t (0 <= t < tiles).
+__device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int32_t* idx, int nblk, int t,
+                                                  int& block, int& nblocks, int& group) {
+  int found = -1;
+  if (t >= s.base && t < s.base + s.count) {
+    int cur = s.in_rs, k = s.base, prev = s.lo > 0 ? block_group(idx, s.lo - 1) : 0;
+    for (int b = s.lo; b < s.hi; ++b) {
+      const int e = block_group(idx, b);
+      if (b == 0 || e != prev) cur = b;
+      prev = e;
+      if (e >= 0 && ((b - cur) & 1) == 0) {
+        if (k == t) { found = b; break; }
+        ++k;
+      }
+    }
+  }
+  const unsigned long long who = __ballot(found >= 0);
+  block = uniform(__shfl(found, __ffsll(who) - 1, kWave));
+  group = uniform(block_group(idx, block));
+  nblocks = (block + 1 < nblk && block_group(idx, block + 1) == group) ? 2 : 1;
+  nblocks = uniform(nblocks);
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N;  // 4 waves: one per SIMD; 8 waves: two per SIMD
@@ -202,20 +284,29 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   int bid = blockIdx.x;
   int split = 0;
   int n_tile, m_tile, group = 0;
-  if constexpr (MODE == kDense) {
+  int tiles_m = p.tiles_m;
+  [[maybe_unused]] ContigScan cs;
+  if constexpr (MODE == kContiguous) {
+    // the grid is sized for the largest possible tile count; workgroups
+    // past the real count have nothing to do
+    cs = contiguous_scan(p.m_indices, p.m / 128);
+    tiles_m = cs.tiles;
+    if (bid >= tiles_m * p.tiles_n) return;
+  }
+  if constexpr (MODE == kDense || MODE == kContiguous) {
     // Workgroups are dispatched to the 8 XCDs round-robin and each XCD has
     // its own L2: give XCD x a contiguous range of logical tiles, walked in
     // groups of kGroupM M-tiles (M fastest), so the tiles an XCD runs at
     // once share a few A and B K-slices.  (A bijection, so correctness does
     // not depend on the dispatch order.)
-    const int total = gridDim.x;
+    const int total = MODE == kContiguous ? tiles_m * p.tiles_n : int(gridDim.x);
     const int xcd = bid % kXcds, slot = bid / kXcds;
     const int per = total / kXcds, extra = total % kXcds;
     int L = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
     if constexpr (SPLIT) { split = L % p.splits; L /= p.splits; }
     const int band = kGroupM * p.tiles_n;
     const int first_m = (L / band) * kGroupM;
-    const int rows_in_band = min(p.tiles_m - first_m, kGroupM);
+    const int rows_in_band = min(tiles_m - first_m, kGroupM);
     const int in_band = L % band;
     m_tile = first_m + in_band % rows_in_band;
     n_tile = in_band / rows_in_band;
@@ -225,7 +316,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
     m_tile = bid % p.tiles_m;
     group = bid / p.tiles_m;  // masked only
   }
-  const int m0 = m_tile * BM, n0 = n_tile * BN;
+  int m0 = m_tile * BM;
+  const int n0 = n_tile * BN;
 
   const uint8_t* A = p.a;
   const float* SA = p.sa;
@@ -234,8 +326,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   uint16_t* OUT = p.out;
   int rows = p.m;
   if constexpr (MODE == kContiguous) {
-    const int gi = p.m_indices[m0];
-    if (gi < 0) return;  // skipped block: output untouched
+    static_assert(BM == 256, "contiguous tiles are one or two 128-row blocks");
+    int block, nblocks, gi;
+    contiguous_locate(cs, p.m_indices, p.m / 128, m_tile, block, nblocks, gi);
+    m0 = 128 * block;
+    rows = m0 + 128 * nblocks;  // rows of other blocks are neither used nor written
     B += int64_t(gi) * p.n * p.k;
     SB += int64_t(gi) * p.nb * p.kg;
   } else if constexpr (MODE == kMasked) {
@@ -306,9 +401,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
     }
   }
   const float* sb_row = sb_cache[wrow_n / 128];
-  // In the masked layout a wave whose tokens are all past the count skips
-  // the products (its copies still run: the ring is shared).
-  const bool wave_live = MODE != kMasked || m0 + wrow_m < rows;
+  // A wave whose tokens are all past the tile's valid rows (masked counts,
+  // one-block contiguous tiles) skips the products (its copies still run:
+  // the ring is shared).
+  const bool wave_live = MODE == kDense || m0 + wrow_m < rows;
 
   // Fragment pointers of ring slot 0 (wave and fragment row offsets are
   // multiples of 16, i.e. whole 2 KB blocks).

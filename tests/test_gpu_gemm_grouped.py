@@ -39,6 +39,42 @@ def test_contiguous_skipped_block_untouched():
     assert_close(got[valid], ref[valid], "contiguous with a skipped block")
 
 
+@pytest.mark.parametrize("pattern", ["odd_runs", "skip_inside_run", "interleaved", "many_blocks"])
+def test_contiguous_tiling_patterns(pattern):
+    """Group runs of odd block counts (one-block tiles), a run cut by a
+    skipped block, groups alternating block by block (as many tiles as
+    blocks), and more blocks than a wave has lanes.  Every valid output is
+    compared; skipped blocks keep the sentinel."""
+    require_gpu()
+    n, k = 264, 384
+    if pattern == "odd_runs":
+        blocks = [0] + [1] * 3 + [2] + [3] * 5 + [4] * 2
+    elif pattern == "skip_inside_run":
+        blocks = [0, 0, 0, -1, 0, 0, 1, -1, -1, 1, 1, 1]
+    elif pattern == "interleaved":
+        blocks = [0, 1, 0, 2, 1, 2, 0, 1, -1, 2, 0]
+    else:
+        rng = np.random.default_rng(7)
+        blocks = []
+        while len(blocks) < 150:
+            blocks += [int(rng.integers(-1, 5))] * int(rng.integers(1, 6))
+        blocks = blocks[:150]
+    G = max(blocks) + 1
+    sizes = [128 * max(1, blocks.count(g)) for g in range(G)]
+    say(f"contiguous tiling {pattern}: {len(blocks)} blocks, G={G}")
+    _, _, qb, sb, _ = contiguous_case(sizes, n, k, seed=len(blocks))
+    M = 128 * len(blocks)
+    x = synth.normal_f32(len(blocks), synth.S_LHS, (M, k))
+    qa, sa = oracle.cast_1x128(x)
+    m_idx = np.repeat(np.asarray(blocks, np.int32), 128)
+    ref = np.full((M, n), SENTINEL, np.uint16)
+    oracle.gemm_contiguous(qa, sa, qb, sb, m_idx, ref)
+    got = run_contiguous(qa, sa, qb, sb, m_idx)
+    valid = m_idx >= 0
+    assert np.all(got[~valid] == SENTINEL), "a skipped block was written"
+    assert_close(got[valid], ref[valid], f"contiguous {pattern}")
+
+
 def test_contiguous_config2_sampled():
     """G=8, n=4096, k=7168, m_g = 128 * U{4..32} (seed 0)."""
     require_gpu()

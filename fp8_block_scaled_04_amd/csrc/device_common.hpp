@@ -72,6 +72,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return uint32_t(uintptr_t((const __attribute__((address_space(3))) void*)p));
 }
 
+// Uniform (per-wave) value: keeps address arithmetic in scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = uint64_t(uintptr_t(p));
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(v >> 32));
+  return reinterpret_cast<const void*>(uintptr_t((uint64_t(hi) << 32) | lo));
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane i's 16 bytes come from
 // sbase + voffset (a wave-uniform 64-bit base plus a per-lane 32-bit offset)
 // and land at LDS address lds_wave_base + 16 * i (gfx950
@@ -81,17 +90,18 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // serialises the prefetch ring.  The callers therefore own the
 // synchronisation: wait_vmcnt<N>() retires the copies in issue order, then a
 // barrier publishes them to the workgroup.  M0 is written here; these kernels
-// use it for nothing else.
+// use it for nothing else.  Both bases must be the same in every lane (they
+// are passed through readfirstlane, which keeps them in scalar registers).
 __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voffset, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds_wave_base), "v"(voffset), "s"(sbase) : "memory");
+               :: "s"(uniform(int(lds_wave_base))), "v"(voffset), "s"(uniform_ptr(sbase)) : "memory");
 }
 
 // Same path with 4 bytes per lane (global_load_lds_dword): lane i's dword
 // lands at LDS address lds_wave_base + 4 * i.
 __device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voffset, uint32_t lds_wave_base) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds_wave_base), "v"(voffset), "s"(sbase) : "memory");
+               :: "s"(uniform(int(lds_wave_base))), "v"(voffset), "s"(uniform_ptr(sbase)) : "memory");
 }
 
 // Device-coherent 16-byte global store / load (sc1: past the per-XCD L2s, so
@@ -115,8 +125,6 @@ __device__ __forceinline__ void wait_coherent(v4f (&t)[8]) {
                :: "memory");
 }
 
-// Uniform (per-wave) value: keeps address arithmetic in scalar registers.
-__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // One 16x16x128 FP8 x FP8 -> FP32 MFMA with zero accumulator input.  The
 // scaled gfx950 form is used with unit E8M0 scales (127 = 2^0), so it is the

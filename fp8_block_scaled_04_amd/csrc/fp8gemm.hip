@@ -75,28 +75,34 @@ int check_ld(int64_t ld, int64_t rows) {
 }
 
 // ---- dense configuration ---------------------------------------------------
-// Kernel shapes: BM tokens x BN outputs per workgroup, wave grid, LDS stages.
-// A wave's accumulator tile is at most 128 x 64 (128 VGPRs): the promotion
-// FMAs need their accumulators in architectural VGPRs.  The large-M shape
-// runs two waves per SIMD (eight per workgroup) so that one wave's LDS and
-// barrier waits are covered by the other's MFMAs.  Small-M shapes are
-// HBM-bound: narrow N tiles and deep rings keep many copies in flight, and
-// when the tile count would leave CUs idle, K is split across workgroups; the
-// last workgroup to finish a tile adds the partial sums in split order.
+// Kernel shapes: BM tokens x BN outputs per workgroup, wave grid, LDS stages,
+// K groups per stage (ku) and waves sharing a sub-tile (wk).  A wave's
+// accumulator tile is at most 128 x 64 (128 VGPRs): the promotion FMAs need
+// their accumulators in architectural VGPRs.  The large-M shape runs two
+// waves per SIMD (eight per workgroup) so that one wave's LDS and barrier
+// waits are covered by the other's MFMAs.  Small-M shapes are HBM-bound:
+// narrow N tiles give enough workgroups; with few tiles per CU each wave
+// multiplies whole 64 x 32 tiles of its own K groups (ku = wk = 4), which
+// keeps more independent MFMAs in flight per stage; with many tiles per CU,
+// several small workgroups share a CU instead.  When the tile count would
+// leave CUs idle, K is split across workgroups; the last workgroup to finish
+// a tile adds the partial sums in split order.
 struct KernelShape {
-  int bm, bn, stages, waves;
+  int bm, bn, stages, waves, ku;
 };
 enum DenseKind { kS64N64 = 0, kS64N128 = 1, kS128N64 = 2, kS128N128 = 3, kBig = 4, kMid = 5, kS64N32 = 6,
-                 kS128N32 = 7, kKinds = 8 };
+                 kS128N32 = 7, kS64N32K4 = 8, kS128N32K2 = 9, kKinds = 10 };
 constexpr KernelShape kShapes[kKinds] = {
-    {64, 64, 4, 4},    // m <= 64
-    {64, 128, 4, 4},
-    {128, 64, 4, 4},   // 64 < m <= 128
-    {128, 128, 3, 4},
-    {256, 256, 2, 8},  // m > 128
-    {256, 128, 3, 4},
-    {64, 32, 4, 4},
-    {128, 32, 4, 4},
+    {64, 64, 4, 4, 1},    // m <= 64
+    {64, 128, 4, 4, 1},
+    {128, 64, 4, 4, 1},   // 64 < m <= 128
+    {128, 128, 3, 4, 1},
+    {256, 256, 2, 8, 1},  // m > 128
+    {256, 128, 3, 4, 1},
+    {64, 32, 4, 4, 1},
+    {128, 32, 4, 4, 1},
+    {64, 32, 3, 4, 4},    // m <= 64, few tiles per CU: four waves, four K groups per stage
+    {128, 32, 3, 4, 2},   // 64 < m <= 128, few tiles per CU
 };
 constexpr int kMaxSplits = 8;  // the split-K fix-up adds at most this many partials
 
@@ -111,8 +117,10 @@ int env_int(const char* name, int fallback) {
 
 DenseConfig dense_config(int m, int n, int k, bool allow_split) {
   DenseConfig c{};
-  c.kind = m <= 64 ? kS64N32 : (m <= 128 ? kS128N32 : kBig);
   const int cus0 = effective_cus();
+  // few 32-column tiles per CU: the K-group-sharing shapes; many: the plain ones
+  const bool few = cdiv(n, 32) < 2 * int64_t(cus0);
+  c.kind = m <= 64 ? (few ? kS64N32K4 : kS64N32) : (m <= 128 ? (few ? kS128N32K2 : kS128N32) : kBig);
   // large M but few 256 x 256 tiles: narrower tiles with split-K fill the CUs
   if (c.kind == kBig && cdiv(m, 256) * cdiv(n, 256) < cus0 / 2) c.kind = kS128N64;
   const int forced = env_int("FP8G_FORCE_CONFIG", -1);  // debugging and tuning only
@@ -125,7 +133,7 @@ DenseConfig dense_config(int m, int n, int k, bool allow_split) {
   c.gps = kg;
   const int64_t tiles = int64_t(c.tiles_m) * c.tiles_n;
   const int cus = effective_cus();
-  const bool can_split = ks.bm * (ks.bn + 4) * 4 <= ks.stages * (ks.bm + ks.bn) * 128;  // staged tile fits the ring
+  const bool can_split = ks.bm * (ks.bn + 4) * 4 <= ks.stages * ks.ku * (ks.bm + ks.bn) * 128;  // staged tile fits the ring
   // Split only when it at least doubles the workgroup count: each split
   // adds a partial-sum round trip through memory at the end of the kernel.
   if (allow_split && can_split && 2 * tiles <= cus + tiles / 2) {
@@ -155,10 +163,10 @@ unsigned next_epoch() {
   return e;
 }
 
-template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT>
+template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT, int KU = 1, int WK = 1>
 void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT>), dim3(unsigned(grid)), dim3(64 * WMW * WNW), 0, s,
-                     p);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT, KU, WK>), dim3(unsigned(grid)),
+                     dim3(64 * WMW * WNW * WK), 0, s, p);
 }
 
 template <bool SPLIT>
@@ -171,6 +179,8 @@ void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
     case kMid: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
     case kS64N32: launch_gemm<64, 32, 2, 2, 4, kDense, SPLIT>(p, grid, s); break;
     case kS128N32: launch_gemm<128, 32, 4, 1, 4, kDense, SPLIT>(p, grid, s); break;
+    case kS64N32K4: launch_gemm<64, 32, 1, 1, 3, kDense, SPLIT, 4, 4>(p, grid, s); break;
+    case kS128N32K2: launch_gemm<128, 32, 2, 1, 3, kDense, SPLIT, 2, 2>(p, grid, s); break;
     default:
       // the 256 x 256 tile cannot stage a split partial (dense_config never
       // asks for it)
@@ -297,12 +307,15 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
   p.masked_m = masked_m;
   p.sa_ld = lhs_scales_ld;
   p.m = max_m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
-  p.tiles_m = int(cdiv(max_m, 256)); p.tiles_n = int(cdiv(n, 128)); p.splits = 1; p.groups_per_split = p.kg;
+  // 128-row tiles: a group's second row tile exits at once when its count
+  // is at most 128 (the usual decode case), so most RHS tiles are read once.
+  p.tiles_m = int(cdiv(max_m, 128)); p.tiles_n = int(cdiv(n, 128)); p.splits = 1; p.groups_per_split = p.kg;
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n * num_groups;
+  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] masked G=%d max_m=%d n=%d k=%d grid=%lld\n", num_groups, max_m, n, k,
                  (long long)grid);
-  launch_gemm<256, 128, 4, 1, 3, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
+  launch_gemm<128, 128, 2, 2, 4, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
   return launched("masked gemm");
 }
 

@@ -70,18 +70,14 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* p0, const uint8_t* p1) {
 
 // Waits until at most `newer` stages of copies issued after the current one
 // are still in flight (`copies` per stage per wave).
-template <int STAGES, int COPIES>
+template <int STAGES, int COPIES, int N = STAGES - 2>
 __device__ __forceinline__ void wait_stage(int newer) {
-  if constexpr (STAGES >= 3) {
-    if (newer >= 1) {
-      if constexpr (STAGES >= 4) {
-        if (newer >= 2) { wait_vmcnt<2 * COPIES>(); return; }
-      }
-      wait_vmcnt<COPIES>();
-      return;
-    }
+  if constexpr (N <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (newer >= N) { wait_vmcnt<N * COPIES>(); return; }
+    wait_stage<STAGES, COPIES, N - 1>(newer);
   }
-  wait_vmcnt<0>();
 }
 
 // Promotion of one 16x16 product: acc += scale * partial (one FMA per output).
@@ -171,6 +167,15 @@ __device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs
 template <int N>
 struct Int { static constexpr int value = N; };
 
+// Calls f(Int<I>{}) for I = B .. E-1 (compile-time unrolled).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(Int<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 // Tiles of the contiguous layout.  Each aligned 128-row block b carries one
 // group index, m_indices[128 b].  A maximal run of blocks with the same
 // non-negative index is cut into tiles of two blocks from its first block on
@@ -253,23 +258,33 @@ __device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int
   nblocks = uniform(nblocks);
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const GemmParams p) {
-  constexpr int NW = WAVES_M * WAVES_N;  // 4 waves: one per SIMD; 8 waves: two per SIMD
+// KU consecutive K groups share one ring stage (one wait and one barrier),
+// and WK waves (dividing KU) may share each sub-tile, taking every WK-th
+// group of a stage; their partial tiles are added in LDS, in wave order,
+// after the K loop.  With few tokens a group's products are too short to
+// cover the fixed latency of a stage's synchronisation and LDS reads; giving
+// each wave its own groups of a larger sub-tile keeps several independent
+// chains of MFMAs in flight.
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT, int KU = 1, int WK = 1>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(const GemmParams p) {
+  constexpr int NW = WAVES_M * WAVES_N * WK;  // 4 waves: one per SIMD; 8 waves: two per SIMD
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
   constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   constexpr int TM = WM / 16, TN = WN / 16;
   static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 sub-tiles");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range stays inside one RHS scale block");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM <= 256, "whole 1 KB copies; scales in one copy");
-  static_assert(STAGES >= 2 && STAGES <= 4, "ring depth");
-  // LDS: [STAGES][BM][128 B] LHS tiles, then [STAGES][BN][128 B] RHS tiles,
-  // then [STAGES][BM] LHS scales, then the tile's RHS scale rows.
+  static_assert(STAGES >= 2 && STAGES <= 8 && KU >= 1 && KU <= 4 && KU % WK == 0, "ring depth");
+  // LDS: [STAGES * KU][BM][128 B] LHS tiles, then [STAGES * KU][BN][128 B]
+  // RHS tiles, then [STAGES * KU][BM] LHS scales (one group per slot, KU
+  // slots per stage), then the tile's RHS scale rows.
+  constexpr int SLOTS = STAGES * KU;
   constexpr int A_BYTES = BM * kRowBytes, B_BYTES = BN * kRowBytes, S_BYTES = BM * 4;
-  constexpr int A_REGION = 0, B_REGION = STAGES * A_BYTES, S_REGION = B_REGION + STAGES * B_BYTES;
-  constexpr int RING = S_REGION + STAGES * S_BYTES;
-  constexpr int A_COPIES = BM / (8 * NW), B_COPIES = BN / (8 * NW);  // 8-row copies per wave per stage
-  static_assert((STAGES - 2) * (A_COPIES + B_COPIES) < 64, "vmcnt range");
+  constexpr int A_REGION = 0, B_REGION = SLOTS * A_BYTES, S_REGION = B_REGION + SLOTS * B_BYTES;
+  constexpr int RING = S_REGION + SLOTS * S_BYTES;
+  constexpr int A_COPIES = BM / (8 * NW), B_COPIES = BN / (8 * NW);  // 8-row copies per wave per group
+  constexpr int STAGE_COPIES = KU * (A_COPIES + B_COPIES);
+  static_assert((STAGES - 2) * STAGE_COPIES < 64, "vmcnt range");
   constexpr int SB_BLOCKS = (BN + 127) / 128;  // RHS scale blocks a tile touches
   static_assert(RING + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS");
 
@@ -278,7 +293,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x >> 6);
-  const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+  const int wk = wave / (WAVES_M * WAVES_N);  // which groups of a stage this wave multiplies
+  const int wm = (wave % (WAVES_M * WAVES_N)) / WAVES_N, wn = wave % WAVES_N;
 
   // ---- work unit ------------------------------------------------------
   int bid = blockIdx.x;
@@ -347,7 +363,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
     g_begin = split * p.groups_per_split;
     g_end = min(p.kg, g_begin + p.groups_per_split);
   }
-  const int niter = g_end - g_begin;
+  const int ngroups = g_end - g_begin;
+  const int niter = (ngroups + KU - 1) / KU;  // ring stages
 
   // ---- HBM -> LDS copies: per-lane byte offsets are loop invariant --------
   // Copy i of this wave fills 1 KB unit u = i * NW + wave of the tile, i.e.
@@ -368,17 +385,25 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   }
   const uint32_t s_off = 4u * uint32_t(min(m0 + 4 * lane, int(p.sa_ld) - 4));
   const uint32_t lds0 = uniform(int(lds_addr(smem)));
-  auto issue = [&](auto slot_tag, int g) {
-    constexpr int slot = decltype(slot_tag)::value;
-    const uint8_t* a_src = A + int64_t(g) * kGroupK;
-    const uint8_t* b_src = B + int64_t(g) * kGroupK;
+  // Stage `it` holds groups g_begin + KU * it + u, u < KU; in a last,
+  // partial stage the missing groups repeat the last one (never multiplied),
+  // so every stage issues the same number of copies.
+  auto issue = [&](auto stage_tag, int it) {
+    constexpr int stage = decltype(stage_tag)::value;
+    static_for<0, KU>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int slot = stage * KU + decltype(uc)::value;
+      const int g = uniform(min(g_begin + KU * it + decltype(uc)::value, g_end - 1));
+      const uint8_t* a_src = A + int64_t(g) * kGroupK;
+      const uint8_t* b_src = B + int64_t(g) * kGroupK;
 #pragma unroll
-    for (int i = 0; i < A_COPIES; ++i)
-      copy16_to_lds(a_src, a_off[i], lds0 + A_REGION + slot * A_BYTES + (i * NW + wave) * 1024);
+      for (int i = 0; i < A_COPIES; ++i)
+        copy16_to_lds(a_src, a_off[i], lds0 + A_REGION + slot * A_BYTES + (i * NW + wave) * 1024);
 #pragma unroll
-    for (int i = 0; i < B_COPIES; ++i)
-      copy16_to_lds(b_src, b_off[i], lds0 + B_REGION + slot * B_BYTES + (i * NW + wave) * 1024);
-    if (wave == 0 && lane < BM / 4) copy16_to_lds(SA + int64_t(g) * p.sa_ld, s_off, lds0 + S_REGION + slot * S_BYTES);
+      for (int i = 0; i < B_COPIES; ++i)
+        copy16_to_lds(b_src, b_off[i], lds0 + B_REGION + slot * B_BYTES + (i * NW + wave) * 1024);
+      if (wave == 0 && lane < BM / 4)
+        copy16_to_lds(SA + int64_t(g) * p.sa_ld, s_off, lds0 + S_REGION + slot * S_BYTES);
+    });
   };
 
   v4f acc[TN][TM];
@@ -393,7 +418,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   // also covers them and the K loop reads them without a global load.
   {
     const uint32_t sb_lds = uniform(int(lds_addr(&sb_cache[0][0])));
-    for (int c = wave; c < SB_BLOCKS * ((niter + 63) / 64); c += NW) {
+    for (int c = wave; c < SB_BLOCKS * ((ngroups + 63) / 64); c += NW) {
       const int b = c % SB_BLOCKS, part = c / SB_BLOCKS;
       const int blk = min(n0 / 128 + b, p.nb - 1);
       const int g = min(g_begin + 64 * part + lane, g_end - 1);
@@ -406,35 +431,66 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
   // the ring is shared).
   const bool wave_live = MODE == kDense || m0 + wrow_m < rows;
 
-  // Fragment pointers of ring slot 0 (wave and fragment row offsets are
+  // Fragment pointers of ring slot wk (wave and fragment row offsets are
   // multiples of 16, i.e. whole 2 KB blocks).
   const int lr = lane & 15, c0 = 2 * (lane >> 4);
   FragPtrs f;
-  f.a0 = smem + A_REGION + wrow_m * kRowBytes + tile_byte(lr, c0);
-  f.a1 = smem + A_REGION + wrow_m * kRowBytes + tile_byte(lr, c0 + 1);
-  f.b0 = smem + B_REGION + wrow_n * kRowBytes + tile_byte(lr, c0);
-  f.b1 = smem + B_REGION + wrow_n * kRowBytes + tile_byte(lr, c0 + 1);
-  f.s = reinterpret_cast<const float*>(smem + S_REGION) + wrow_m + lr;
+  f.a0 = smem + A_REGION + wk * A_BYTES + wrow_m * kRowBytes + tile_byte(lr, c0);
+  f.a1 = smem + A_REGION + wk * A_BYTES + wrow_m * kRowBytes + tile_byte(lr, c0 + 1);
+  f.b0 = smem + B_REGION + wk * B_BYTES + wrow_n * kRowBytes + tile_byte(lr, c0);
+  f.b1 = smem + B_REGION + wk * B_BYTES + wrow_n * kRowBytes + tile_byte(lr, c0 + 1);
+  f.s = reinterpret_cast<const float*>(smem + S_REGION + wk * S_BYTES) + wrow_m + lr;
 
-  if (0 < niter) issue(Int<0>{}, g_begin);  // (the scale-row copies above are older)
-  if constexpr (STAGES > 2) if (1 < niter) issue(Int<1>{}, g_begin + 1);
-  if constexpr (STAGES > 3) if (2 < niter) issue(Int<2>{}, g_begin + 2);
+  // (the scale-row copies above are older)
+  static_for<0, STAGES - 1>([&](auto ic) __attribute__((always_inline)) {
+    constexpr int I = decltype(ic)::value;
+    if (I < niter) issue(Int<I>{}, I);
+  });
 
-  auto step = [&](auto slot_tag, int it) {
-    constexpr int slot = decltype(slot_tag)::value;
-    wait_stage<STAGES, A_COPIES + B_COPIES>(min(STAGES - 2, niter - 1 - it));
+  auto step = [&](auto stage_tag, int it) {
+    constexpr int stage = decltype(stage_tag)::value;
+    wait_stage<STAGES, STAGE_COPIES>(min(STAGES - 2, niter - 1 - it));
     wait_lgkmcnt0();
     block_barrier();
-    if (it + STAGES - 1 < niter) issue(Int<(slot + STAGES - 1) % STAGES>{}, g_begin + it + STAGES - 1);
+    if (it + STAGES - 1 < niter) issue(Int<(stage + STAGES - 1) % STAGES>{}, it + STAGES - 1);
     if (wave_live)
-      group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES>(acc, f, sb_row[it]);
+      static_for<0, KU / WK>([&](auto uc) __attribute__((always_inline)) {
+        constexpr int slot = stage * KU + decltype(uc)::value * WK;  // + wk, folded into f
+        const int gl = KU * it + decltype(uc)::value * WK + wk;
+        if (KU == 1 || gl < ngroups)
+          group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES>(acc, f, sb_row[gl]);
+      });
   };
   for (int it = 0; it < niter; it += STAGES) {
-    step(Int<0>{}, it);
-    if (it + 1 < niter) step(Int<1 % STAGES>{}, it + 1);
-    if constexpr (STAGES > 2) if (it + 2 < niter) step(Int<2 % STAGES>{}, it + 2);
-    if constexpr (STAGES > 3) if (it + 3 < niter) step(Int<3 % STAGES>{}, it + 3);
+    static_for<0, STAGES>([&](auto ic) __attribute__((always_inline)) {
+      constexpr int I = decltype(ic)::value;
+      if (it + I < niter) step(Int<I>{}, it + I);
+    });
   }
+
+  // ---- waves sharing a sub-tile add their partial tiles (wave order) ------
+  if constexpr (WK > 1) {
+    constexpr int PART = TN * TM * kWave;  // v4f elements of one wave's sub-tile
+    static_assert(NW * PART * 16 <= RING, "partial tiles fit in the ring");
+    v4f* red = reinterpret_cast<v4f*>(smem);
+    __syncthreads();  // every wave is done with the ring
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int j = 0; j < TM; ++j) red[(wave * TN + i) * TM * kWave + j * kWave + lane] = acc[i][j];
+    __syncthreads();
+    if (wk == 0) {
+#pragma unroll
+      for (int w = 1; w < WK; ++w) {
+        const int other = w * WAVES_M * WAVES_N + wave;
+#pragma unroll
+        for (int i = 0; i < TN; ++i)
+#pragma unroll
+          for (int j = 0; j < TM; ++j) acc[i][j] += red[(other * TN + i) * TM * kWave + j * kWave + lane];
+      }
+    }
+  }
+  const bool holder = wk == 0;  // the waves that now hold the tile's sums
 
   // ---- epilogue: lane holds n = col..col+3 of one token per sub-tile -------
   if constexpr (SPLIT) {
@@ -450,13 +506,15 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
     constexpr int LDT = BN + 4;  // padded row stride (floats) of the staged tile
     constexpr int CHUNKS = BM * BN / 4;
     float* stage = reinterpret_cast<float*>(smem);
-    __syncthreads();  // every wave is done with the ring
+    __syncthreads();  // every wave is done with the ring (and with the partial-tile sums)
+    if (holder) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i)
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j)
-        *reinterpret_cast<v4f*>(stage + (wrow_m + 16 * j + (lane & 15)) * LDT + wrow_n + 16 * i + 4 * (lane >> 4)) =
-            acc[i][j];
+        for (int j = 0; j < TM; ++j)
+          *reinterpret_cast<v4f*>(stage + (wrow_m + 16 * j + (lane & 15)) * LDT + wrow_n + 16 * i + 4 * (lane >> 4)) =
+              acc[i][j];
+    }
     __syncthreads();
     const int64_t mn = int64_t(p.m) * p.n;
     for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
@@ -506,6 +564,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_kernel(const G
       }
     }
   } else {
+    if (!holder) return;
 #pragma unroll
     for (int i = 0; i < TN; ++i) {
       const int col = n0 + wrow_n + 16 * i + 4 * (lane >> 4);

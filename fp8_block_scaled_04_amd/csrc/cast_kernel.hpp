@@ -50,31 +50,41 @@ __device__ __forceinline__ void load8(const uint16_t* x, float v[8]) {
   }
 }
 
-// Per-token-group cast.  Grid (ceil(m / 16), KG), 256 threads: 16 lanes per
-// (row, group), 8 consecutive elements per lane.  Scales are written
-// MN-major, scales[g * ld + row], 16 consecutive rows per workgroup.
-template <typename T>
+// Per-token-group cast.  Grid (ceil(m / 16), ceil(KG / G)), 256 threads: 16
+// lanes per (row, group), 8 consecutive elements per lane, G consecutive K
+// groups per workgroup with all of their loads issued before any is used.
+// Scales are written MN-major, scales[g * ld + row], 16 consecutive rows
+// per workgroup.
+template <typename T, int G>
 __global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x, int m, int k,
                                                          uint8_t* __restrict__ q,
                                                          float* __restrict__ scales, int64_t ld) {
   const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int g = blockIdx.y;
-  const int col = g * 128 + (threadIdx.x & 15) * 8;
-  const bool live = row < m && col < k;
-  float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  if (live) load8(x + int64_t(row) * k + col, v);
-  float amax = 0.f;
+  const int g0 = blockIdx.y * G;
+  float v[G][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  for (int u = 0; u < G; ++u) {
+    const int col = (g0 + u) * 128 + (threadIdx.x & 15) * 8;
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-  const float s = group_scale(amax);
-  if (live) {
-    uint2 w;
-    w.x = e4m3x4(__fdiv_rn(v[0], s), __fdiv_rn(v[1], s), __fdiv_rn(v[2], s), __fdiv_rn(v[3], s));
-    w.y = e4m3x4(__fdiv_rn(v[4], s), __fdiv_rn(v[5], s), __fdiv_rn(v[6], s), __fdiv_rn(v[7], s));
-    *reinterpret_cast<uint2*>(q + int64_t(row) * k + col) = w;
-    if ((threadIdx.x & 15) == 0) scales[int64_t(g) * ld + row] = s;
+    for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+    if (row < m && col < k) load8(x + int64_t(row) * k + col, v[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < G; ++u) {
+    const int col = (g0 + u) * 128 + (threadIdx.x & 15) * 8;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+    const float s = group_scale(amax);
+    if (row < m && col < k) {
+      uint2 w;
+      w.x = e4m3x4(__fdiv_rn(v[u][0], s), __fdiv_rn(v[u][1], s), __fdiv_rn(v[u][2], s), __fdiv_rn(v[u][3], s));
+      w.y = e4m3x4(__fdiv_rn(v[u][4], s), __fdiv_rn(v[u][5], s), __fdiv_rn(v[u][6], s), __fdiv_rn(v[u][7], s));
+      *reinterpret_cast<uint2*>(q + int64_t(row) * k + col) = w;
+      if ((threadIdx.x & 15) == 0) scales[int64_t(g0 + u) * ld + row] = s;
+    }
   }
 }
 

@@ -330,14 +330,26 @@ int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k, uint8_t* 
   if (scales_ld < m) return FP8G_EUNSUPPORTED;
   const int64_t kg = cdiv(k, 128);
   if (kg > 65535) return FP8G_EUNSUPPORTED;
-  const dim3 grid(unsigned(cdiv(m, 16)), unsigned(kg));
+  // two K groups per workgroup once there are many (long rows of a large
+  // activation): fewer, longer workgroups keep more loads in flight
+  const bool pair = kg >= 64;
+  const dim3 grid(unsigned(cdiv(m, 16)), unsigned(pair ? cdiv(kg, 2) : kg));
   auto s = static_cast<hipStream_t>(stream);
-  if (x_dtype == FP8G_F32)
-    hipLaunchKernelGGL(fp8g::cast_1x128_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(x), m, k,
-                       q, scales, scales_ld);
-  else
-    hipLaunchKernelGGL(fp8g::cast_1x128_kernel<uint16_t>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                       m, k, q, scales, scales_ld);
+  if (x_dtype == FP8G_F32) {
+    if (pair)
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<float, 2>), grid, dim3(256), 0, s, static_cast<const float*>(x), m,
+                         k, q, scales, scales_ld);
+    else
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<float, 1>), grid, dim3(256), 0, s, static_cast<const float*>(x), m,
+                         k, q, scales, scales_ld);
+  } else {
+    if (pair)
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<uint16_t, 2>), grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), m, k, q, scales, scales_ld);
+    else
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<uint16_t, 1>), grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), m, k, q, scales, scales_ld);
+  }
   return launched("per-token-group cast");
 }
 

@@ -26,7 +26,8 @@ def gpu_cast_1x128(x_host, ld=None):
     return q.cpu().numpy(), s.cpu().numpy()
 
 
-@pytest.mark.parametrize("m,k", [(1, 128), (16, 128), (37, 1000), (64, 7168), (300, 2048), (4096, 7168)])
+@pytest.mark.parametrize("m,k", [(1, 128), (16, 128), (37, 1000), (64, 7168), (300, 2048), (4096, 7168),
+                                 (19, 8200), (40, 16384)])
 def test_cast_1x128_f32_bit_exact(m, k):
     require_gpu()
     say(f"cast_1x128 f32 m={m} k={k}")
@@ -42,7 +43,7 @@ def test_cast_1x128_f32_bit_exact(m, k):
     assert np.all(s[:, m:] == -7.0)        # padding columns of the scales untouched
 
 
-@pytest.mark.parametrize("m,k", [(5, 256), (128, 7168)])
+@pytest.mark.parametrize("m,k", [(5, 256), (128, 7168), (9, 8320)])
 def test_cast_1x128_bf16_bit_exact(m, k):
     require_gpu()
     say(f"cast_1x128 bf16 m={m} k={k}")

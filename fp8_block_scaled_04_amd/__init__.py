@@ -10,4 +10,6 @@ from .binding import (  # noqa: F401
     Fp8GemmError, fp8_cast_per_block, fp8_cast_per_token_group, fp8_gemm_nt,
     fp8_gemm_workspace_bytes, fp8_get_num_cus, fp8_grouped_gemm_contiguous,
     fp8_grouped_gemm_masked, fp8_set_num_cus, fp8_status_string,
+    fp8_moe_contiguous_rows, fp8_moe_gather_rows, fp8_moe_layout_contiguous, fp8_moe_layout_masked,
+    fp8_moe_layout_workspace_bytes, fp8_moe_scatter_rows,
 )

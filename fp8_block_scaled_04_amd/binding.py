@@ -39,6 +39,12 @@ _SIGNATURES = {
     "fp8_set_num_cus": ([_i32], _i32),
     "fp8_get_num_cus": ([], _i32),
     "fp8_status_string": ([_i32], ctypes.c_char_p),
+    "fp8_moe_contiguous_rows": ([_i32, _i32], _i32),
+    "fp8_moe_layout_workspace_bytes": ([_i32, _i32], _sz),
+    "fp8_moe_layout_contiguous": ([_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp], _i32),
+    "fp8_moe_layout_masked": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "fp8_moe_scatter_rows": ([_vp, _vp, _i64, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
+    "fp8_moe_gather_rows": ([_vp, _i32, _i32, _vp, _i32, _vp, _vp], _i32),
 }
 
 
@@ -206,3 +212,85 @@ def fp8_get_num_cus() -> int:
 
 def fp8_status_string(status: int) -> str:
     return status_string(status)
+
+
+# ---- MoE layout steps ----------------------------------------------------------
+def fp8_moe_contiguous_rows(num_tokens: int, num_groups: int) -> int:
+    return int(lib().fp8_moe_contiguous_rows(int(num_tokens), int(num_groups)))
+
+
+def fp8_moe_layout_workspace_bytes(num_tokens: int, num_groups: int) -> int:
+    return int(lib().fp8_moe_layout_workspace_bytes(int(num_tokens), int(num_groups)))
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(1, (nbytes + 3) // 4), dtype=torch.int32, device=device)
+
+
+def fp8_moe_layout_contiguous(expert_idx, num_groups, m_rows=None, workspace=None, stream=None):
+    """Contiguous (prefill) layout of a routing.  Returns (counts [G],
+    offsets [G+1], dst_row [T], m_indices [m_rows]) as int32 device tensors."""
+    expert_idx = _i32t(expert_idx, "expert_idx")
+    T = expert_idx.numel()
+    G = int(num_groups)
+    if m_rows is None:
+        m_rows = fp8_moe_contiguous_rows(T, G)
+    dev = expert_idx.device
+    counts = torch.empty(G, dtype=torch.int32, device=dev)
+    offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
+    dst = torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T]
+    m_indices = torch.empty(max(int(m_rows), 1), dtype=torch.int32, device=dev)[:int(m_rows)]
+    if workspace is None:
+        workspace = _workspace(fp8_moe_layout_workspace_bytes(T, G), dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fp8_moe_layout_contiguous(_p(expert_idx), T, G, _p(counts), _p(offsets), _p(dst), _p(m_indices),
+                                         int(m_rows), _p(workspace), ws_bytes, _stream(stream))
+    _check("fp8_moe_layout_contiguous", st)
+    return counts, offsets, dst, m_indices
+
+
+def fp8_moe_layout_masked(expert_idx, num_groups, max_m, workspace=None, stream=None):
+    """Masked (decode) layout of a routing.  Returns (counts [G], dst_row [T],
+    masked_m [G]) as int32 device tensors."""
+    expert_idx = _i32t(expert_idx, "expert_idx")
+    T = expert_idx.numel()
+    G = int(num_groups)
+    dev = expert_idx.device
+    counts = torch.empty(G, dtype=torch.int32, device=dev)
+    masked_m = torch.empty(G, dtype=torch.int32, device=dev)
+    dst = torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T]
+    if workspace is None:
+        workspace = _workspace(fp8_moe_layout_workspace_bytes(T, G), dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().fp8_moe_layout_masked(_p(expert_idx), T, G, int(max_m), _p(counts), _p(dst), _p(masked_m),
+                                     _p(workspace), ws_bytes, _stream(stream))
+    _check("fp8_moe_layout_masked", st)
+    return counts, dst, masked_m
+
+
+def fp8_moe_scatter_rows(q, scales, dst_row, q_out, scales_out, rows_per_group=None, stream=None):
+    """q [T][k] codes and scales [KG][ld >= T] to their laid-out rows.
+    Contiguous: q_out [M][k], scales_out [KG][ld >= M].  Masked: q_out
+    [G][max_m][k], scales_out [G][KG][ld >= max_m] (rows_per_group = max_m)."""
+    q, q_out = _codes(q, "q"), _codes(q_out, "q_out")
+    scales, scales_out = _f32(scales, "scales"), _f32(scales_out, "scales_out")
+    dst_row = _i32t(dst_row, "dst_row")
+    T, k = q.shape
+    out_rows = q_out.numel() // k if k else 0
+    if rows_per_group is None:
+        rows_per_group = q_out.shape[-2] if q_out.dim() == 3 else out_rows
+    st = lib().fp8_moe_scatter_rows(_p(q), _p(scales), scales.shape[-1], T, k, _p(dst_row), int(rows_per_group),
+                                    int(out_rows), _p(q_out), _p(scales_out), scales_out.shape[-1], _stream(stream))
+    _check("fp8_moe_scatter_rows", st)
+    return q_out, scales_out
+
+
+def fp8_moe_gather_rows(y, dst_row, out, stream=None):
+    """out[t] = y[dst_row[t]] (bfloat16 rows), zeros where dst_row[t] < 0."""
+    y, out = _bf16(y, "y"), _bf16(out, "out")
+    dst_row = _i32t(dst_row, "dst_row")
+    n = out.shape[-1]
+    y_rows = y.numel() // n if n else 0
+    st = lib().fp8_moe_gather_rows(_p(y), n, y_rows, _p(dst_row), dst_row.numel(), _p(out), _stream(stream))
+    _check("fp8_moe_gather_rows", st)
+    return out

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libfp8gemm.so")
-SOURCES = [os.path.join(CSRC, "fp8gemm.hip")]
+SOURCES = [os.path.join(CSRC, "fp8gemm.hip"), os.path.join(CSRC, "moe.hip")]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -1,0 +1,179 @@
+// MoE layout steps around the grouped GEMMs, for gfx950.
+//
+// What is computed (the kwkr.cn DeepGEMM usage article, section 3.2 and the
+// section 4.3 flow: order the tokens by expert index, count each expert's
+// tokens, run the grouped GEMM, put the outputs back in token order; the
+// contiguous and masked layouts of "DeepSeek open-source week, day 3:
+// DeepGEMM"):
+//   counts[g]  = number of tokens routed to expert g;
+//   rank[t]    = number of earlier tokens routed to the same expert (the
+//                sort is stable, so the layout is unique);
+//   contiguous: offsets[g + 1] = offsets[g] + ceil(counts[g] / 128) * 128,
+//               dst[t] = offsets[e[t]] + rank[t], m_indices = expert of each
+//               row (-1 past the last expert);
+//   masked:     dst[t] = e[t] * max_m + rank[t] if rank[t] < max_m else -1,
+//               masked_m[g] = min(counts[g], max_m).
+// A stable counting sort in three passes: per-chunk histograms, a scan over
+// chunks and experts, then ranks within each chunk.  No atomics decide an
+// order: LDS atomics only count.
+#pragma once
+
+#include "device_common.hpp"
+
+namespace fp8g {
+
+constexpr int kMoeChunk = 1024;      // tokens per workgroup in the counting passes
+constexpr int kMoeMaxGroups = 1024;  // experts the layout kernels handle
+constexpr int kMoeAlign = 128;       // the contiguous GEMM's row block
+
+__device__ __forceinline__ bool routed(int e, int G) { return e >= 0 && e < G; }
+
+// Pass 1: hist[b][g] = tokens of chunk b routed to g.  Grid: chunks; 256 threads.
+__global__ void __launch_bounds__(256) moe_hist_kernel(const int32_t* __restrict__ expert, int T, int G,
+                                                       int32_t* __restrict__ hist) {
+  __shared__ int cnt[kMoeMaxGroups];
+  for (int g = threadIdx.x; g < G; g += blockDim.x) cnt[g] = 0;
+  __syncthreads();
+  const int t0 = blockIdx.x * kMoeChunk;
+  for (int i = threadIdx.x; i < kMoeChunk; i += blockDim.x) {
+    const int t = t0 + i;
+    if (t < T) {
+      const int e = expert[t];
+      if (routed(e, G)) atomicAdd(&cnt[e], 1);
+    }
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < G; g += blockDim.x) hist[int64_t(blockIdx.x) * G + g] = cnt[g];
+}
+
+// Pass 2, one workgroup of 1024 threads: replaces hist[b][g] by the tokens
+// of g in chunks before b, writes the totals, the aligned offsets
+// (contiguous) and the kept counts (masked).
+__global__ void __launch_bounds__(1024) moe_scan_kernel(int32_t* __restrict__ hist, int B, int G,
+                                                        int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ masked_m, int max_m) {
+  __shared__ int part[1024];
+  const int g = threadIdx.x;
+  int total = 0;
+  if (g < G) {
+    for (int b = 0; b < B; ++b) {
+      const int c = hist[int64_t(b) * G + g];
+      hist[int64_t(b) * G + g] = total;
+      total += c;
+    }
+    counts[g] = total;
+    if (masked_m) masked_m[g] = min(total, max_m);
+  }
+  if (!offsets) return;
+  // exclusive scan of the aligned sizes over the experts (Hillis-Steele)
+  part[g] = g < G ? (total + kMoeAlign - 1) / kMoeAlign * kMoeAlign : 0;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = g >= d ? part[g - d] : 0;
+    __syncthreads();
+    part[g] += v;
+    __syncthreads();
+  }
+  if (g < G) offsets[g + 1] = part[g];
+  if (g == 0) offsets[0] = 0;
+}
+
+// Pass 3: destinations.  Grid: chunks; 1024 threads = 16 waves, wave w
+// takes tokens [64 w, 64 w + 64) of the chunk.  rank = (tokens of the same
+// expert in earlier chunks) + (in earlier waves of this chunk) + (in earlier
+// lanes of this wave).
+template <bool CONTIGUOUS>
+__global__ void __launch_bounds__(1024) moe_dest_kernel(const int32_t* __restrict__ expert, int T, int G,
+                                                        const int32_t* __restrict__ hist,
+                                                        const int32_t* __restrict__ offsets, int max_m,
+                                                        int32_t* __restrict__ dst) {
+  constexpr int NW = kMoeChunk / kWave;
+  __shared__ int wave_cnt[NW][kMoeMaxGroups];
+  for (int i = threadIdx.x; i < NW * G; i += blockDim.x) wave_cnt[i / G][i % G] = 0;
+  __syncthreads();
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kMoeChunk + threadIdx.x;
+  const int e = t < T ? expert[t] : -1;
+  const bool ok = routed(e, G);
+  int in_wave = 0;  // earlier lanes of this wave with the same expert
+  for (int j = 0; j < kWave; ++j) {
+    const int ej = __shfl(e, j, kWave);
+    if (j < lane && ej == e) ++in_wave;
+  }
+  if (ok) atomicAdd(&wave_cnt[wave][e], 1);
+  __syncthreads();
+  if (t >= T) return;
+  if (!ok) {
+    dst[t] = -1;
+    return;
+  }
+  int rank = hist[int64_t(blockIdx.x) * G + e] + in_wave;
+  for (int w = 0; w < wave; ++w) rank += wave_cnt[w][e];
+  if (CONTIGUOUS) dst[t] = offsets[e] + rank;
+  else dst[t] = rank < max_m ? e * max_m + rank : -1;
+}
+
+// m_indices[r] = the expert whose aligned block range holds r, -1 past the
+// last one.  Grid-stride over rows; the offsets are searched in LDS.
+__global__ void __launch_bounds__(256) moe_row_groups_kernel(const int32_t* __restrict__ offsets, int G, int rows,
+                                                             int32_t* __restrict__ m_indices) {
+  __shared__ int off[kMoeMaxGroups + 1];
+  for (int g = threadIdx.x; g <= G; g += blockDim.x) off[g] = offsets[g];
+  __syncthreads();
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += gridDim.x * blockDim.x) {
+    int v = -1;
+    if (r < off[G]) {
+      int lo = 0, hi = G - 1;  // last g with off[g] <= r
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      v = lo;
+    }
+    m_indices[r] = v;
+  }
+}
+
+// Moves token t's E4M3 row and its KG scales to laid-out row dst[t].  One
+// wave per token, 16-byte copies (k % 16 == 0).  Scales: source MN-major
+// [KG][ld_in]; destination row d lives in group d / rpg at row d % rpg of
+// that group's MN-major [KG][ld_out] block.
+__global__ void __launch_bounds__(256) moe_scatter_kernel(const uint8_t* __restrict__ q,
+                                                          const float* __restrict__ scales, int64_t ld_in,
+                                                          int T, int k, const int32_t* __restrict__ dst,
+                                                          int rpg, int out_rows, uint8_t* __restrict__ q_out,
+                                                          float* __restrict__ scales_out, int64_t ld_out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int d = dst[t];
+  if (d < 0 || d >= out_rows) return;
+  const v4i* src = reinterpret_cast<const v4i*>(q + int64_t(t) * k);
+  v4i* out = reinterpret_cast<v4i*>(q_out + int64_t(d) * k);
+  for (int c = lane; c < k / 16; c += kWave) out[c] = src[c];
+  const int kg = (k + 127) / 128;
+  float* so = scales_out + int64_t(d / rpg) * kg * ld_out + (d % rpg);
+  for (int g = lane; g < kg; g += kWave) so[int64_t(g) * ld_out] = scales[int64_t(g) * ld_in + t];
+}
+
+// out[t] = y[dst[t]] (BF16 rows, n % 8 == 0), zeros where dst[t] < 0.  One
+// wave per token.
+__global__ void __launch_bounds__(256) moe_gather_kernel(const uint16_t* __restrict__ y, int n, int y_rows,
+                                                         const int32_t* __restrict__ dst, int T,
+                                                         uint16_t* __restrict__ out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int d = dst[t];
+  v4i* o = reinterpret_cast<v4i*>(out + int64_t(t) * n);
+  if (d < 0 || d >= y_rows) {
+    for (int c = lane; c < n / 8; c += kWave) o[c] = v4i{0, 0, 0, 0};
+    return;
+  }
+  const v4i* src = reinterpret_cast<const v4i*>(y + int64_t(d) * n);
+  for (int c = lane; c < n / 8; c += kWave) o[c] = src[c];
+}
+
+}  // namespace fp8g

@@ -132,6 +132,68 @@ int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
 int fp8_cast_per_block(const float* w, int n, int k,
                        uint8_t* q, float* scales, void* stream);
 
+/* ---- MoE layout steps around the grouped GEMMs -----------------------------
+ * The flow of the kwkr.cn DeepGEMM usage article (section 3.2; section 4.3:
+ * order the tokens by expert index, count each expert's tokens, run the
+ * grouped GEMM, put the outputs back in token order), producing the two
+ * grouped layouts of "DeepSeek open-source week, day 3: DeepGEMM".  Token t
+ * is routed to expert expert_idx[t]; an index outside [0, num_groups) routes
+ * it nowhere.  rank[t] = number of earlier tokens routed to the same expert
+ * (a stable order, so every output below is unique).  num_groups <= 1024.
+ * All arrays are int32 device arrays (4-byte aligned).  The layout calls
+ * need a caller workspace of fp8_moe_layout_workspace_bytes() bytes; it
+ * needs no initialisation and is not shared by concurrent calls. */
+
+/* Rows that always suffice for the contiguous layout of num_tokens tokens
+ * over num_groups experts (each expert pads to a multiple of 128); -1 on bad
+ * arguments.  Host-only. */
+int fp8_moe_contiguous_rows(int num_tokens, int num_groups);
+size_t fp8_moe_layout_workspace_bytes(int num_tokens, int num_groups);
+
+/* Contiguous layout (MoE prefill):
+ *   counts[G]        tokens per expert
+ *   offsets[G + 1]   offsets[g + 1] = offsets[g] + ceil(counts[g] / 128) * 128
+ *   dst_row[T]       offsets[e] + rank[t], or -1 for an unrouted token
+ *   m_indices[m_rows] expert of each laid-out row (its padding rows too),
+ *                    -1 from offsets[G] on: the input of
+ *                    fp8_grouped_gemm_contiguous (m_total = m_rows).
+ * m_rows must be at least fp8_moe_contiguous_rows(T, G) (FP8G_EINVAL
+ * otherwise).  Padding rows receive no token: fill them (e.g. with zero
+ * codes) before the GEMM if their outputs are to be defined. */
+int fp8_moe_layout_contiguous(const int32_t* expert_idx, int num_tokens, int num_groups,
+                              int32_t* counts, int32_t* offsets, int32_t* dst_row,
+                              int32_t* m_indices, int m_rows,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Masked layout (MoE decode): a slot of max_m rows per expert.
+ *   counts[G]    tokens per expert
+ *   dst_row[T]   e * max_m + rank[t] when rank[t] < max_m, else -1 (the
+ *                token does not fit its expert's slot and is dropped)
+ *   masked_m[G]  min(counts[g], max_m): the input of fp8_grouped_gemm_masked */
+int fp8_moe_layout_masked(const int32_t* expert_idx, int num_tokens, int num_groups, int max_m,
+                          int32_t* counts, int32_t* dst_row, int32_t* masked_m,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Moves each token's E4M3 row and its scales to its laid-out row d =
+ * dst_row[t] (tokens with d < 0 or d >= out_rows stay put):
+ *   q [T][k] codes, scales MN-major [KG][scales_ld >= T] (the cast's output);
+ *   q_out [out_rows][k]; scales_out: row d sits in group d / rows_per_group,
+ *   at row d % rows_per_group of that group's MN-major
+ *   [KG][scales_out_ld >= rows_per_group] block.  Contiguous layout:
+ *   rows_per_group = out_rows (one block); masked layout: rows_per_group =
+ *   max_m, out_rows = G * max_m.  k % 16 == 0; q and q_out 16-byte aligned.
+ * Rows no token lands on are not written. */
+int fp8_moe_scatter_rows(const uint8_t* q, const float* scales, int64_t scales_ld,
+                         int num_tokens, int k, const int32_t* dst_row,
+                         int rows_per_group, int out_rows,
+                         uint8_t* q_out, float* scales_out, int64_t scales_out_ld, void* stream);
+
+/* Puts the GEMM's BF16 rows back in token order: out[t] = y[dst_row[t]]
+ * (out [T][n], y [y_rows][n]); a row of zeros where dst_row[t] < 0 or
+ * >= y_rows.  n % 8 == 0; y and out 16-byte aligned. */
+int fp8_moe_gather_rows(const uint16_t* y, int n, int y_rows, const int32_t* dst_row,
+                        int num_tokens, uint16_t* out, void* stream);
+
 /* Workspace bytes that let fp8_gemm_nt choose split-K for this shape
  * (0 = never needed).  An upper bound; depends on the CU limit in force. */
 size_t fp8_gemm_workspace_bytes(int m, int n, int k, int num_groups);

@@ -219,3 +219,8 @@ def tolerance_check(gpu_bits, ref_bits, rtol=8e-3, atol_rms=1e-2):
     ratio = np.abs(g - r) / np.where(bound > 0, bound, 1.0)
     worst = float(ratio.max())
     return bool(worst <= 1.0), worst, rms
+
+
+# MoE layout steps (plain numpy, see moe.py)
+from .moe import (moe_contiguous_rows, moe_counts, moe_gather_rows, moe_layout_contiguous,  # noqa: E402,F401
+                  moe_layout_masked, moe_ranks, moe_scatter_rows)

@@ -495,8 +495,16 @@ def cpu_baseline(shapes, host, target_s):
             flop += 2.0 * r * n * k
         return flop, t
 
-    f0, t0 = run(8)
-    rows = int(max(8, min(max(m for m, _, _ in shapes), 8 * target_s / max(t0, 1e-3))))
+    # calibrate twice: tiny samples are dominated by fixed costs
+    mmax = max(m for m, _, _ in shapes)
+    rows = 8
+    for _ in range(2):
+        _, t0 = run(rows)
+        nxt = int(max(8, min(mmax, rows * 0.5 * target_s / max(t0, 1e-3))))
+        if nxt <= rows:
+            break
+        rows = nxt
+    rows = int(max(8, min(mmax, rows * target_s / max(run(rows)[1], 1e-3))))
     flop, t = run(rows)
     return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"first {rows} rows (all rows if fewer) of every shape, cast + GEMM: "

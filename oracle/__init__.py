@@ -60,17 +60,19 @@ def _load():
     lib.orc_bf16_rne.argtypes = [ctypes.c_double]
     lib.orc_bf16_rne.restype = ctypes.c_uint16
     lib.orc_bf16_rne_array.argtypes = [_f64p, _i64, _u16p]
-    lib.orc_cast_1x128_f32.argtypes = [_f32p, _i64, _i64, _u8p, _f32p, _int]
-    lib.orc_cast_1x128_bf16.argtypes = [_u16p, _i64, _i64, _u8p, _f32p, _int]
-    lib.orc_cast_128x128_f32.argtypes = [_f32p, _i64, _i64, _u8p, _f32p, _int]
+    lib.orc_fp8_table.argtypes = [_int, _f64p]
+    lib.orc_fp8_encode_array.argtypes = [_int, _f64p, _i64, _u8p]
+    lib.orc_cast_1x128_f32.argtypes = [_f32p, _i64, _i64, _u8p, _f32p, _int, _int]
+    lib.orc_cast_1x128_bf16.argtypes = [_u16p, _i64, _i64, _u8p, _f32p, _int, _int]
+    lib.orc_cast_128x128_f32.argtypes = [_f32p, _i64, _i64, _u8p, _f32p, _int, _int]
     lib.orc_gemm_nt.argtypes = [_u8p, _f32p, _u8p, _f32p, _i64, _i64, _i64,
-                                _u16p, _vp, _int]
+                                _u16p, _vp, _int, _int, _int]
     lib.orc_gemm_contiguous.argtypes = [_u8p, _f32p, _u8p, _f32p, _i32p, _i64,
                                         _i64, _i64, _i64, _u16p, _vp, _int]
     lib.orc_gemm_masked.argtypes = [_u8p, _f32p, _u8p, _f32p, _i32p, _i64,
                                     _i64, _i64, _i64, _u16p, _vp, _int]
     lib.orc_gemm_points.argtypes = [_u8p, _f32p, _u8p, _f32p, _i64, _i64p,
-                                    _i64p, _i64, _u16p, _vp, _int]
+                                    _i64p, _i64, _u16p, _vp, _int, _int, _int]
     lib.orc_hardware_threads.restype = _int
     _lib = lib
     return lib
@@ -94,6 +96,26 @@ def _pre_ptr(pre):
 
 def kg_of(k: int) -> int:
     return (int(k) + 127) // 128
+
+
+E4M3, E5M2 = 0, 1  # FP8 formats
+
+
+def fp8_table(fmt=E4M3) -> np.ndarray:
+    """Value of each of the 256 codes of the format (E4M3FN: NaN for 0x7F and
+    0xFF; E5M2: +-inf for 0x7C / 0xFC, NaN for 0x7D-0x7F and 0xFD-0xFF)."""
+    out = np.empty(256, np.float64)
+    _load().orc_fp8_table(int(fmt), out)
+    return out
+
+
+def fp8_encode(x, fmt=E4M3) -> np.ndarray:
+    """Round to the nearest code of the format, ties to even, saturating at
+    its largest finite value (448 or 57344)."""
+    xa = _c(np.asarray(x, np.float64).ravel(), np.float64)
+    q = np.empty(xa.size, np.uint8)
+    _load().orc_fp8_encode_array(int(fmt), xa, xa.size, q)
+    return q.reshape(np.shape(x))
 
 
 # --------------------------------------------------------------------------
@@ -120,7 +142,7 @@ def bf16_rne(x) -> np.ndarray:
     return out.reshape(np.shape(x))
 
 
-def cast_1x128(x, nthreads=None):
+def cast_1x128(x, nthreads=None, fmt=E4M3):
     """Per-token-group cast: x [m][k] fp32 (or uint16 bf16 bits) ->
     (codes uint8 [m][k], scales fp32 [m][KG])."""
     x = np.asarray(x)
@@ -128,31 +150,32 @@ def cast_1x128(x, nthreads=None):
     q = np.empty((m, k), np.uint8)
     s = np.empty((m, kg_of(k)), np.float32)
     if x.dtype == np.uint16:
-        _load().orc_cast_1x128_bf16(_c(x, np.uint16), m, k, q, s, _threads(nthreads))
+        _load().orc_cast_1x128_bf16(_c(x, np.uint16), m, k, q, s, _threads(nthreads), int(fmt))
     else:
-        _load().orc_cast_1x128_f32(_c(x, np.float32), m, k, q, s, _threads(nthreads))
+        _load().orc_cast_1x128_f32(_c(x, np.float32), m, k, q, s, _threads(nthreads), int(fmt))
     return q, s
 
 
-def cast_128x128(w, nthreads=None):
+def cast_128x128(w, nthreads=None, fmt=E4M3):
     """128x128 block cast: w [n][k] fp32 -> (codes [n][k], scales [NB][KG])."""
     w = _c(w, np.float32)
     n, k = w.shape
     q = np.empty((n, k), np.uint8)
     s = np.empty(((n + 127) // 128, kg_of(k)), np.float32)
-    _load().orc_cast_128x128_f32(w, n, k, q, s, _threads(nthreads))
+    _load().orc_cast_128x128_f32(w, n, k, q, s, _threads(nthreads), int(fmt))
     return q, s
 
 
-def gemm_nt(A, sa, B, sb, want_pre=False, nthreads=None):
-    """Dense NT GEMM -> bf16 bits [m][n] (and the FP64 pre-rounding values)."""
+def gemm_nt(A, sa, B, sb, want_pre=False, nthreads=None, a_fmt=E4M3, b_fmt=E4M3):
+    """Dense NT GEMM -> bf16 bits [m][n] (and the FP64 pre-rounding values).
+    a_fmt / b_fmt: the operands' FP8 formats."""
     A = _c(A, np.uint8); B = _c(B, np.uint8)
     m, k = A.shape
     n = B.shape[0]
     out = np.empty((m, n), np.uint16)
     pre = np.empty((m, n), np.float64) if want_pre else None
     _load().orc_gemm_nt(A, _c(sa, np.float32), B, _c(sb, np.float32), m, n, k,
-                        out, _pre_ptr(pre), _threads(nthreads))
+                        out, _pre_ptr(pre), _threads(nthreads), int(a_fmt), int(b_fmt))
     return (out, pre) if want_pre else out
 
 
@@ -184,7 +207,7 @@ def gemm_masked(A, sa, B, sb, masked_m, out, want_pre=False, nthreads=None):
     return pre
 
 
-def gemm_points(A, sa, B, sb, rows, cols, want_pre=False, nthreads=None):
+def gemm_points(A, sa, B, sb, rows, cols, want_pre=False, nthreads=None, a_fmt=E4M3, b_fmt=E4M3):
     """Selected outputs (rows[p], cols[p]) of A . B^T for one RHS."""
     A = _c(A, np.uint8); B = _c(B, np.uint8)
     k = A.shape[-1]
@@ -194,7 +217,7 @@ def gemm_points(A, sa, B, sb, rows, cols, want_pre=False, nthreads=None):
     pre = np.empty(rows.size, np.float64) if want_pre else None
     _load().orc_gemm_points(A.reshape(-1, k), _c(sa, np.float32).reshape(A.reshape(-1, k).shape[0], -1),
                             B.reshape(-1, k), _c(sb, np.float32), k, rows, cols,
-                            rows.size, out, _pre_ptr(pre), _threads(nthreads))
+                            rows.size, out, _pre_ptr(pre), _threads(nthreads), int(a_fmt), int(b_fmt))
     return (out, pre) if want_pre else out
 
 

@@ -19,12 +19,20 @@
 //   [DG-usage]    kwkr.cn DeepGEMM usage article: §3.1 and the code in §4.2
 //                 (scale = amax / 448, q = fp8(x / scale)).
 //   [DG-practice] "DeepGEMM: FP8 GEMM kernel optimisation practice on Hopper
-//                 Tensor Cores" (jianying88.com): §5.2 (per-group scaling,
-//                 128 elements per group), §6.3-6.4 (K tails).
+//                 Tensor Cores" (jianying88.com): §1.3 (A and B in E4M3 or
+//                 E5M2, configurable), §3.1 (E4M3: 4 exponent / 3 mantissa
+//                 bits, max about 448; E5M2: 5 / 2 bits, max about 57344),
+//                 §5.2 (per-group scaling, 128 elements per group), §6.3-6.4
+//                 (K tails).
 //
 // Readings where the pages are silent (each also listed in the design notes):
-//   * FP8 is OCP E4M3FN: no infinities, NaN = S.1111.111, max 448.
-//   * Encoding rounds to nearest, ties to even, and saturates at +-448.
+//   * FP8 is OCP E4M3FN: no infinities, NaN = S.1111.111, max 448; the second
+//     format is OCP E5M2: infinities S.11111.00, NaN S.11111.xx (xx != 0),
+//     max 57344.
+//   * Encoding rounds to nearest, ties to even, and saturates at the format's
+//     largest finite value (+-448, +-57344).
+//   * A cast to E5M2 uses scale = amax / 57344, the rule amax / 448 with the
+//     format's own maximum.
 //   * An all-zero group or block gets scale 1.0f (codes all zero).
 //   * The cast divides with IEEE fp32 correctly rounded division.
 //   * K groups are [128g, 128g+128); the last one may be partial.  N blocks
@@ -62,23 +70,48 @@ double e4m3_value(unsigned code) {
   return s ? -mag : mag;
 }
 
+// ---- E5M2 decode, closed form ([DG-practice] §3.1; OCP E5M2) ---------------
+// sign s, exponent e (5 bits, bias 15), mantissa f (2 bits).
+//   e = 31, f = 0 : infinity;  e = 31, f != 0 : NaN
+//   e = 0         : subnormal, f * 2^-16
+//   otherwise     : (4 + f) * 2^(e - 17)   (= 1.f * 2^(e-15))
+double e5m2_value(unsigned code) {
+  const unsigned s = (code >> 7) & 1u, e = (code >> 2) & 31u, f = code & 3u;
+  double mag;
+  if (e == 31u) mag = f == 0u ? HUGE_VAL : std::nan("");
+  else mag = (e == 0u) ? std::ldexp(double(f), -16) : std::ldexp(double(4u + f), int(e) - 17);
+  return s ? -mag : mag;
+}
+
+// Formats: 0 = E4M3FN, 1 = E5M2.
+constexpr int kE4M3 = 0, kE5M2 = 1;
+
 struct Table {
   double v[256];
-  Table() { for (unsigned c = 0; c < 256; ++c) v[c] = e4m3_value(c); }
+  uint8_t max_code;  // largest finite non-negative code
+  explicit Table(int fmt) {
+    for (unsigned c = 0; c < 256; ++c) v[c] = fmt == kE5M2 ? e5m2_value(c) : e4m3_value(c);
+    max_code = fmt == kE5M2 ? 0x7B : 0x7E;
+  }
 };
-const Table& table() { static const Table t; return t; }
+const Table& table(int fmt = kE4M3) {
+  static const Table t4(kE4M3), t5(kE5M2);
+  return fmt == kE5M2 ? t5 : t4;
+}
 
-// ---- E4M3FN encode: nearest finite magnitude, ties to even, saturating ----
-// The 127 non-negative finite codes 0x00..0x7E are strictly increasing in
-// value, so the nearest one is found by bisection on that sorted list.
-uint8_t e4m3_encode(double x) {
+// ---- encode: nearest finite magnitude, ties to even, saturating ------------
+// The non-negative finite codes 0x00..max_code are strictly increasing in
+// value (both formats), so the nearest one is found by bisection on that
+// sorted list.  NaN encodes as 0x7F (a NaN in both formats).
+uint8_t fp8_encode(double x, int fmt) {
   if (std::isnan(x)) return 0x7F;
   const uint8_t sign = std::signbit(x) ? 0x80 : 0x00;
   const double a = std::fabs(x);
-  const double* v = table().v;
-  if (a >= v[0x7E]) return uint8_t(sign | 0x7E);
+  const Table& tb = table(fmt);
+  const double* v = tb.v;
+  if (a >= v[tb.max_code]) return uint8_t(sign | tb.max_code);
   // largest code lo with v[lo] <= a  (v[0] = 0 <= a always holds)
-  int lo = 0, hi = 0x7E;
+  int lo = 0, hi = tb.max_code;
   while (hi - lo > 1) {
     const int mid = (lo + hi) / 2;
     if (v[mid] <= a) lo = mid; else hi = mid;
@@ -90,6 +123,7 @@ uint8_t e4m3_encode(double x) {
   }
   return uint8_t(sign | c);
 }
+uint8_t e4m3_encode(double x) { return fp8_encode(x, kE4M3); }
 
 // ---- BF16 round-to-nearest-even, straight from double ----------------------
 // Keeps 8 significant bits (quantum 2^(e-8) for a in [2^(e-1), 2^e)); below
@@ -134,15 +168,19 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   S_g(i, j) = sum_{t in K group g} dec(A[i][t]) * dec(B[j][t]).
 // Each S_g is exact in FP64 (every E4M3 value is a multiple of 2^-9 below
 // 2^9, so a 128-term sum of products is a multiple of 2^-18 below 2^43).
+// (With E5M2 operands the values are multiples of 2^-16 below 2^16, so the
+// products and their 128-term sums stay exact as well.)
 double gemm_element(const uint8_t* a_row, const float* sa_row,
-                    const uint8_t* b_row, const float* sb_row, int64_t k) {
-  const double* v = table().v;
+                    const uint8_t* b_row, const float* sb_row, int64_t k,
+                    int a_fmt = kE4M3, int b_fmt = kE4M3) {
+  const double* va = table(a_fmt).v;
+  const double* vb = table(b_fmt).v;
   const int64_t kg = ceil_div(k, 128);
   double acc = 0.0;
   for (int64_t g = 0; g < kg; ++g) {
     const int64_t t0 = g * 128, t1 = std::min<int64_t>(t0 + 128, k);
     double s = 0.0;
-    for (int64_t t = t0; t < t1; ++t) s += v[a_row[t]] * v[b_row[t]];
+    for (int64_t t = t0; t < t1; ++t) s += va[a_row[t]] * vb[b_row[t]];
     acc += (double(sa_row[g]) * double(sb_row[g])) * s;
   }
   return acc;
@@ -151,12 +189,12 @@ double gemm_element(const uint8_t* a_row, const float* sa_row,
 // Rows [r0, r1) of D = A . B^T with one RHS (B, sb) for every row.
 void gemm_rows(const uint8_t* A, const float* sa, const uint8_t* B,
                const float* sb, int64_t n, int64_t k, int64_t r0, int64_t r1,
-               uint16_t* out, double* pre) {
+               uint16_t* out, double* pre, int a_fmt = kE4M3, int b_fmt = kE4M3) {
   const int64_t kg = ceil_div(k, 128);
   for (int64_t i = r0; i < r1; ++i)
     for (int64_t j = 0; j < n; ++j) {
       const double d = gemm_element(A + i * k, sa + i * kg, B + j * k,
-                                    sb + (j / 128) * kg, k);
+                                    sb + (j / 128) * kg, k, a_fmt, b_fmt);
       out[i * n + j] = bf16_from_double(d);
       if (pre) pre[i * n + j] = d;
     }
@@ -164,9 +202,9 @@ void gemm_rows(const uint8_t* A, const float* sa, const uint8_t* B,
 
 // Per-group amax -> scale -> codes, for one group of `len` elements spread
 // with stride `stride` ([DG-usage] §3.1/§4.2; [DG-practice] §5.2).
-float group_scale(float amax) {
+float group_scale(float amax, int fmt = kE4M3) {
   if (amax == 0.0f) return 1.0f;  // reading: an all-zero group keeps codes 0
-  return amax / 448.0f;           // IEEE fp32, correctly rounded
+  return amax / (fmt == kE5M2 ? 57344.0f : 448.0f);  // IEEE fp32, correctly rounded
 }
 
 }  // namespace
@@ -184,6 +222,14 @@ void orc_e4m3_encode_array(const double* x, int64_t count, uint8_t* q) {
   for (int64_t i = 0; i < count; ++i) q[i] = e4m3_encode(x[i]);
 }
 
+// The same two for either format (0 = E4M3FN, 1 = E5M2).
+void orc_fp8_table(int fmt, double* out256) {
+  for (int c = 0; c < 256; ++c) out256[c] = table(fmt).v[c];
+}
+void orc_fp8_encode_array(int fmt, const double* x, int64_t count, uint8_t* q) {
+  for (int64_t i = 0; i < count; ++i) q[i] = fp8_encode(x[i], fmt);
+}
+
 uint16_t orc_bf16_rne(double x) { return bf16_from_double(x); }
 
 void orc_bf16_rne_array(const double* x, int64_t count, uint16_t* out) {
@@ -193,7 +239,7 @@ void orc_bf16_rne_array(const double* x, int64_t count, uint16_t* out) {
 // Per-token-group cast of an fp32 [m][k] matrix: one scale per row and per
 // 128-wide K group.  q [m][k] codes, scales [m][KG] (logical layout).
 void orc_cast_1x128_f32(const float* x, int64_t m, int64_t k, uint8_t* q,
-                        float* scales, int nthreads) {
+                        float* scales, int nthreads, int fmt) {
   const int64_t kg = ceil_div(k, 128);
   parallel_rows(m, nthreads, [&](int64_t r0, int64_t r1) {
     for (int64_t i = r0; i < r1; ++i)
@@ -201,11 +247,11 @@ void orc_cast_1x128_f32(const float* x, int64_t m, int64_t k, uint8_t* q,
         const int64_t t0 = g * 128, t1 = std::min<int64_t>(t0 + 128, k);
         float amax = 0.0f;
         for (int64_t t = t0; t < t1; ++t) amax = std::max(amax, std::fabs(x[i * k + t]));
-        const float s = group_scale(amax);
+        const float s = group_scale(amax, fmt);
         scales[i * kg + g] = s;
         for (int64_t t = t0; t < t1; ++t) {
           const float y = x[i * k + t] / s;
-          q[i * k + t] = e4m3_encode(double(y));
+          q[i * k + t] = fp8_encode(double(y), fmt);
         }
       }
   });
@@ -213,19 +259,19 @@ void orc_cast_1x128_f32(const float* x, int64_t m, int64_t k, uint8_t* q,
 
 // Same, for bf16 input (bit patterns); each value widens exactly to fp32.
 void orc_cast_1x128_bf16(const uint16_t* x, int64_t m, int64_t k, uint8_t* q,
-                         float* scales, int nthreads) {
+                         float* scales, int nthreads, int fmt) {
   std::vector<float> xf(size_t(m * k));
   for (int64_t i = 0; i < m * k; ++i) {
     const uint32_t u = uint32_t(x[i]) << 16;
     std::memcpy(&xf[size_t(i)], &u, 4);
   }
-  orc_cast_1x128_f32(xf.data(), m, k, q, scales, nthreads);
+  orc_cast_1x128_f32(xf.data(), m, k, q, scales, nthreads, fmt);
 }
 
 // Block cast of an fp32 [n][k] weight: one scale per 128x128 block, the
 // edge blocks using only their real elements.  scales [NB][KG].
 void orc_cast_128x128_f32(const float* w, int64_t n, int64_t k, uint8_t* q,
-                          float* scales, int nthreads) {
+                          float* scales, int nthreads, int fmt) {
   const int64_t kg = ceil_div(k, 128), nb = ceil_div(n, 128);
   parallel_rows(nb, nthreads, [&](int64_t b0, int64_t b1) {
     for (int64_t b = b0; b < b1; ++b)
@@ -235,12 +281,12 @@ void orc_cast_128x128_f32(const float* w, int64_t n, int64_t k, uint8_t* q,
         float amax = 0.0f;
         for (int64_t i = i0; i < i1; ++i)
           for (int64_t t = t0; t < t1; ++t) amax = std::max(amax, std::fabs(w[i * k + t]));
-        const float s = group_scale(amax);
+        const float s = group_scale(amax, fmt);
         scales[b * kg + g] = s;
         for (int64_t i = i0; i < i1; ++i)
           for (int64_t t = t0; t < t1; ++t) {
             const float y = w[i * k + t] / s;
-            q[i * k + t] = e4m3_encode(double(y));
+            q[i * k + t] = fp8_encode(double(y), fmt);
           }
       }
   });
@@ -249,11 +295,12 @@ void orc_cast_128x128_f32(const float* w, int64_t n, int64_t k, uint8_t* q,
 // Dense NT GEMM: A [m][k], sa [m][KG], B [n][k], sb [NB][KG] -> out [m][n]
 // bf16 bits.  `pre` (optional, [m][n]) receives the FP64 value before the
 // BF16 rounding.
+// a_fmt / b_fmt: the operands' formats (0 = E4M3FN, 1 = E5M2).
 void orc_gemm_nt(const uint8_t* A, const float* sa, const uint8_t* B,
                  const float* sb, int64_t m, int64_t n, int64_t k,
-                 uint16_t* out, double* pre, int nthreads) {
+                 uint16_t* out, double* pre, int nthreads, int a_fmt, int b_fmt) {
   parallel_rows(m, nthreads, [&](int64_t r0, int64_t r1) {
-    gemm_rows(A, sa, B, sb, n, k, r0, r1, out, pre);
+    gemm_rows(A, sa, B, sb, n, k, r0, r1, out, pre, a_fmt, b_fmt);
   });
 }
 
@@ -301,13 +348,13 @@ void orc_gemm_masked(const uint8_t* A, const float* sa, const uint8_t* B,
 void orc_gemm_points(const uint8_t* A, const float* sa, const uint8_t* B,
                      const float* sb, int64_t k, const int64_t* rows,
                      const int64_t* cols, int64_t npts, uint16_t* out,
-                     double* pre, int nthreads) {
+                     double* pre, int nthreads, int a_fmt, int b_fmt) {
   const int64_t kg = ceil_div(k, 128);
   parallel_rows(npts, nthreads, [&](int64_t p0, int64_t p1) {
     for (int64_t p = p0; p < p1; ++p) {
       const int64_t i = rows[p], j = cols[p];
       const double d = gemm_element(A + i * k, sa + i * kg, B + j * k,
-                                    sb + (j / 128) * kg, k);
+                                    sb + (j / 128) * kg, k, a_fmt, b_fmt);
       out[p] = bf16_from_double(d);
       if (pre) pre[p] = d;
     }

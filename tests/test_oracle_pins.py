@@ -530,3 +530,112 @@ def test_tolerance_check_catches_a_planted_error():
     assert oracle.tolerance_check(oracle.bf16_rne(fine), ref_bits)[0]
     nan = ref.copy(); nan[3] = np.nan
     assert not oracle.tolerance_check(oracle.bf16_rne(nan), ref_bits)[0]
+
+
+# ---- E5M2 (the second format: "DeepGEMM: FP8 GEMM kernel optimisation
+# practice on Hopper Tensor Cores" §1.3 and the §3.1 table) ---------------------
+def torch_e5m2_values(codes):
+    t = torch.tensor(np.asarray(codes, np.uint8)).view(torch.float8_e5m2)
+    return t.to(torch.float64).numpy()
+
+
+def torch_e5m2_encode(x):
+    """torch's float32 -> float8_e5m2 conversion (round to nearest even)."""
+    t = torch.tensor(np.asarray(x, np.float32)).to(torch.float8_e5m2)
+    return t.view(torch.uint8).numpy()
+
+
+def test_e5m2_decode_closed_forms_and_torch():
+    t = oracle.fp8_table(oracle.E5M2)
+    assert t[0x7B] == 57344.0 and t[0x04] == 2.0 ** -14 and t[0x01] == 2.0 ** -16 and t[0x3C] == 1.0
+    assert np.isposinf(t[0x7C]) and np.isneginf(t[0xFC])
+    assert np.all(np.isnan(t[[0x7D, 0x7E, 0x7F, 0xFD, 0xFE, 0xFF]]))
+    assert np.all(np.diff(t[:0x7C]) > 0)
+    ref = torch_e5m2_values(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(t), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    assert np.array_equal(t[fin], ref[fin])
+    # the E4M3 table is unchanged by the format argument
+    assert np.array_equal(oracle.fp8_table(oracle.E4M3), oracle.e4m3_table(), equal_nan=True)
+
+
+def test_e5m2_encode_roundtrip_midpoints_saturation():
+    t = oracle.fp8_table(oracle.E5M2)
+    codes = np.array([c for c in range(256) if np.isfinite(t[c])], np.uint8)
+    assert np.array_equal(oracle.fp8_encode(t[codes], oracle.E5M2), codes)
+    for c in range(0, 0x7B):
+        mid = (t[c] + t[c + 1]) / 2
+        want = c if c % 2 == 0 else c + 1
+        assert oracle.fp8_encode([mid], oracle.E5M2)[0] == want, hex(c)
+    q = oracle.fp8_encode([57344.0, 61439.0, 61440.0, 1e30, np.inf, -7e4, np.nan], oracle.E5M2)
+    assert list(q) == [0x7B, 0x7B, 0x7B, 0x7B, 0x7B, 0xFB, 0x7F]
+
+
+def test_e5m2_encode_matches_torch_and_bruteforce():
+    rng = np.random.default_rng(2)
+    t = oracle.fp8_table(oracle.E5M2)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 3000,
+        np.exp(rng.uniform(np.log(1e-7), np.log(57000.0), 20000)) * rng.choice([-1, 1], 20000),
+    ]).astype(np.float32)
+    mids = ((t[:0x7B] + t[1:0x7C]) / 2).astype(np.float32)
+    near = np.concatenate([np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e5))])
+    x = np.concatenate([x, near, -near, mids]).astype(np.float32)
+    x = x[np.abs(x) <= 57344.0]  # torch's conversion is not saturating past the maximum
+    ours = oracle.fp8_encode(x.astype(np.float64), oracle.E5M2)
+    assert np.array_equal(ours, torch_e5m2_encode(x))
+    fin = [(Fraction(float(t[c])), c) for c in range(0x7C)]
+    for idx in range(0, x.size, 97):
+        v = x[idx]
+        a = Fraction(float(abs(v)))
+        best = min(fin, key=lambda p: (abs(p[0] - a), p[1] % 2))
+        assert ours[idx] == best[1] | (0x80 if np.signbit(v) else 0)
+
+
+def test_e5m2_cast_matches_torch_reference():
+    """The cast with the E5M2 maximum, against the usage-article cast code
+    (amax / max, x / scale, convert) run with torch on the CPU."""
+    x = synth.normal_f32(3, 1, (29, 700))
+    x[4, :] = 0.0
+    q, s = oracle.cast_1x128(x, fmt=oracle.E5M2)
+    xt = torch.tensor(x)
+    kg = s.shape[1]
+    for g in range(kg):
+        blk = xt[:, 128 * g:128 * g + 128]
+        amax = blk.abs().amax(dim=1)
+        sc = torch.where(amax == 0, torch.ones_like(amax), amax / 57344.0)
+        assert np.array_equal(s[:, g], sc.numpy())
+        y = (blk / sc[:, None]).to(torch.float8_e5m2).view(torch.uint8).numpy()
+        assert np.array_equal(q[:, 128 * g:128 * g + 128], y)
+    wq, ws = oracle.cast_128x128(synth.normal_f32(4, 2, (200, 260)), fmt=oracle.E5M2)
+    assert ws.shape == (2, 3) and np.all((wq & 0x7F) <= 0x7B)
+
+
+@pytest.mark.parametrize("a_fmt,b_fmt", [(1, 1), (0, 1), (1, 0)])
+def test_e5m2_gemm_bruteforce_rational(a_fmt, b_fmt):
+    """Mixed and pure E5M2 operands: exact rational sums (partial K group
+    and N block), decoded through torch's own format tables."""
+    rng = np.random.default_rng(10 + a_fmt * 2 + b_fmt)
+    m, n, k = 3, 130, 259
+    kg, nb = 3, 2
+
+    def codes(fmt, shape):
+        c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+        if fmt == 1:
+            c[(c & 0x7C) == 0x7C] &= 0xF3        # no inf / NaN codes
+        else:
+            c[(c & 0x7F) == 0x7F] &= 0xFE
+        return c
+
+    A, B = codes(a_fmt, (m, k)), codes(b_fmt, (n, k))
+    sa = rng.standard_normal((m, kg)).astype(np.float32)
+    sb = rng.standard_normal((nb, kg)).astype(np.float32)
+    out = oracle.gemm_nt(A, sa, B, sb, a_fmt=a_fmt, b_fmt=b_fmt)
+    dec = {0: torch_e4m3_values, 1: torch_e5m2_values}
+    va = [[Fraction(float(v)) for v in dec[a_fmt](row)] for row in A]
+    vb = [[Fraction(float(v)) for v in dec[b_fmt](row)] for row in B]
+    for i in range(m):
+        for j in range(0, n, 3):
+            tot = sum(va[i][t] * Fraction(float(sa[i, t // 128])) * vb[j][t] * Fraction(float(sb[j // 128, t // 128]))
+                      for t in range(k))
+            assert out[i, j] == bf16_nearest_exact(tot), (i, j)

@@ -25,6 +25,7 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fp8gemm.h")
 
 FP8G_OK, FP8G_EINVAL, FP8G_EUNSUPPORTED, FP8G_ELAUNCH = 0, -1, -2, -3
 FP8G_F32, FP8G_BF16 = 0, 1
+FP8G_E4M3, FP8G_E5M2 = 0, 1
 
 _lib = None
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
@@ -35,6 +36,9 @@ _SIGNATURES = {
     "fp8_grouped_gemm_masked": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "fp8_cast_per_token_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
     "fp8_cast_per_block": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
+    "fp8_gemm_nt_fmt": ([_vp, _i32, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
+    "fp8_cast_per_token_group_fmt": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
+    "fp8_cast_per_block_fmt": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "fp8_gemm_workspace_bytes": ([_i32, _i32, _i32, _i32], _sz),
     "fp8_set_num_cus": ([_i32], _i32),
     "fp8_get_num_cus": ([], _i32),
@@ -95,11 +99,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _codes(t, name):
-    if t.dtype == torch.float8_e4m3fn:
+_FMT_DTYPES = {FP8G_E4M3: torch.float8_e4m3fn, FP8G_E5M2: torch.float8_e5m2}
+_FMT_NAMES = {FP8G_E4M3: "E4M3", FP8G_E5M2: "E5M2"}
+
+
+def _fmt(fmt, name):
+    if fmt not in _FMT_DTYPES:
+        raise ValueError(f"{name} must be FP8G_E4M3 or FP8G_E5M2, got {fmt!r}")
+    return fmt
+
+
+def _codes(t, name, fmt=FP8G_E4M3):
+    if t.dtype == _FMT_DTYPES[fmt]:
         t = t.view(torch.uint8)
     if t.dtype != torch.uint8:
-        raise TypeError(f"{name} must hold E4M3 codes (uint8 or float8_e4m3fn), got {t.dtype}")
+        raise TypeError(f"{name} must hold {_FMT_NAMES[fmt]} codes (uint8 or {_FMT_DTYPES[fmt]}), got {t.dtype}")
     return _dev(t, name)
 
 
@@ -145,6 +159,21 @@ def fp8_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace=None, stream=No
     return out
 
 
+def fp8_gemm_nt_fmt(lhs, lhs_format, lhs_scales, rhs, rhs_format, rhs_scales, out, workspace=None, stream=None):
+    """fp8_gemm_nt with each operand's format given (FP8G_E4M3 or FP8G_E5M2)."""
+    lhs_format, rhs_format = _fmt(lhs_format, "lhs_format"), _fmt(rhs_format, "rhs_format")
+    lhs, rhs = _codes(lhs, "lhs", lhs_format), _codes(rhs, "rhs", rhs_format)
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out = _bf16(out, "out")
+    m, k = lhs.shape
+    n = rhs.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fp8_gemm_nt_fmt(_p(lhs), lhs_format, _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), rhs_format,
+                               _p(rhs_scales), _p(out), m, n, k, _p(workspace), ws_bytes, _stream(stream))
+    _check("fp8_gemm_nt_fmt", st)
+    return out
+
+
 def fp8_grouped_gemm_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices, stream=None):
     """Contiguous-layout grouped GEMM: lhs [M][k], rhs [G][n][k], m_indices [M]."""
     lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
@@ -185,6 +214,35 @@ def fp8_cast_per_token_group(x, q, scales, stream=None):
     m, k = x.shape
     st = lib().fp8_cast_per_token_group(_p(x), dt, m, k, _p(q), _p(scales), scales.shape[-1], _stream(stream))
     _check("fp8_cast_per_token_group", st)
+    return q, scales
+
+
+def fp8_cast_per_token_group_fmt(x, q_format, q, scales, stream=None):
+    """fp8_cast_per_token_group to q_format (FP8G_E4M3 or FP8G_E5M2)."""
+    q_format = _fmt(q_format, "q_format")
+    x = _dev(x, "x")
+    if x.dtype == torch.float32:
+        dt = FP8G_F32
+    elif x.dtype == torch.bfloat16:
+        dt = FP8G_BF16
+    else:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    q, scales = _codes(q, "q", q_format), _f32(scales, "scales")
+    m, k = x.shape
+    st = lib().fp8_cast_per_token_group_fmt(_p(x), dt, q_format, m, k, _p(q), _p(scales), scales.shape[-1],
+                                            _stream(stream))
+    _check("fp8_cast_per_token_group_fmt", st)
+    return q, scales
+
+
+def fp8_cast_per_block_fmt(w, q_format, q, scales, stream=None):
+    """fp8_cast_per_block to q_format (FP8G_E4M3 or FP8G_E5M2)."""
+    q_format = _fmt(q_format, "q_format")
+    w = _f32(w, "w")
+    q, scales = _codes(q, "q", q_format), _f32(scales, "scales")
+    n, k = w.shape
+    st = lib().fp8_cast_per_block_fmt(_p(w), q_format, n, k, _p(q), _p(scales), _stream(stream))
+    _check("fp8_cast_per_block_fmt", st)
     return q, scales
 
 

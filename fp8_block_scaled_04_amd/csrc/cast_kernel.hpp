@@ -1,14 +1,16 @@
-// FP8 E4M3 casts for gfx950: per-token-group (1 x 128, activations) and per
-// 128 x 128 block (weights).
+// FP8 casts for gfx950: per-token-group (1 x 128, activations) and per
+// 128 x 128 block (weights), to E4M3 (the default) or E5M2.
 //
 // What is computed (kwkr.cn DeepGEMM usage article, section 3.1 and the code
 // in section 4.2; "DeepSeek open-source week, day 3: DeepGEMM", "Basic usage"
 // scale shapes): amax = max |x| over the group or block, scale =
 // fl32(amax / 448) (1.0 for an all-zero group, a reading the pages leave
-// open), q = E4M3(fl32(x / scale)).  Division is IEEE fp32 correctly rounded
-// (no reciprocal shortcut), so codes and scales are reproducible bit for bit.
-// The hardware conversion rounds to nearest-even; values are first clamped to
-// +-448, so the conversion saturates instead of producing NaN above 464.
+// open), q = E4M3(fl32(x / scale)); for E5M2 output 57344 (that format's
+// maximum) takes the place of 448.  Division is IEEE fp32 correctly rounded
+// (no reciprocal shortcut), so codes and scales are reproducible bit for
+// bit.  The hardware conversion rounds to nearest-even; values are first
+// clamped to the format's maximum, so the conversion saturates instead of
+// producing NaN or infinity past it.
 //
 // Both kernels are HBM-bound (5 B moved per element, a handful of ALU ops):
 // 16-byte loads, one wave-local amax reduction, packed stores.
@@ -18,18 +20,34 @@
 
 namespace fp8g {
 
+// Largest finite value of the output format: E4M3 448, E5M2 57344 (the
+// "DeepGEMM: FP8 GEMM kernel optimisation practice" page, section 3.1).
+template <int FMT>
+__device__ __forceinline__ constexpr float fmt_max() { return FMT == kFmtE5M2 ? 57344.0f : 448.0f; }
+
+template <int FMT = kFmtE4M3>
 __device__ __forceinline__ float group_scale(float amax) {
-  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, 448.0f);
+  return amax == 0.0f ? 1.0f : __fdiv_rn(amax, fmt_max<FMT>());
 }
 
-// Four fp32 -> four E4M3 codes in one dword (element 0 in the low byte).
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+// Four fp32 -> four codes in one dword (element 0 in the low byte), after a
+// clamp to the format's largest finite value (the conversion would give
+// NaN or infinity past it).
+template <int FMT = kFmtE4M3>
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d) {
+  constexpr float M = fmt_max<FMT>();
+  a = __builtin_amdgcn_fmed3f(a, -M, M);
+  b = __builtin_amdgcn_fmed3f(b, -M, M);
+  c = __builtin_amdgcn_fmed3f(c, -M, M);
+  d = __builtin_amdgcn_fmed3f(d, -M, M);
+  int w;
+  if constexpr (FMT == kFmtE5M2) {
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_bf8_f32(c, d, w, true);
+  } else {
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  }
   return uint32_t(w);
 }
 
@@ -55,7 +73,7 @@ __device__ __forceinline__ void load8(const uint16_t* x, float v[8]) {
 // groups per workgroup with all of their loads issued before any is used.
 // Scales are written MN-major, scales[g * ld + row], 16 consecutive rows
 // per workgroup.
-template <typename T, int G>
+template <typename T, int G, int FMT = kFmtE4M3>
 __global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x, int m, int k,
                                                          uint8_t* __restrict__ q,
                                                          float* __restrict__ scales, int64_t ld) {
@@ -77,11 +95,11 @@ __global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x
     for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[u][i]));
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-    const float s = group_scale(amax);
+    const float s = group_scale<FMT>(amax);
     if (row < m && col < k) {
       uint2 w;
-      w.x = e4m3x4(__fdiv_rn(v[u][0], s), __fdiv_rn(v[u][1], s), __fdiv_rn(v[u][2], s), __fdiv_rn(v[u][3], s));
-      w.y = e4m3x4(__fdiv_rn(v[u][4], s), __fdiv_rn(v[u][5], s), __fdiv_rn(v[u][6], s), __fdiv_rn(v[u][7], s));
+      w.x = fp8x4<FMT>(__fdiv_rn(v[u][0], s), __fdiv_rn(v[u][1], s), __fdiv_rn(v[u][2], s), __fdiv_rn(v[u][3], s));
+      w.y = fp8x4<FMT>(__fdiv_rn(v[u][4], s), __fdiv_rn(v[u][5], s), __fdiv_rn(v[u][6], s), __fdiv_rn(v[u][7], s));
       *reinterpret_cast<uint2*>(q + int64_t(row) * k + col) = w;
       if ((threadIdx.x & 15) == 0) scales[int64_t(g0 + u) * ld + row] = s;
     }
@@ -91,6 +109,7 @@ __global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x
 // 128 x 128 block cast.  Grid (NB, KG), 256 threads.  Each load instruction
 // of a wave covers two 512-byte row segments (32 lanes x 16 B); a thread
 // holds 16 rows x 4 columns.  k must be a multiple of 4.
+template <int FMT = kFmtE4M3>
 __global__ void __launch_bounds__(256) cast_128x128_kernel(const float* __restrict__ w, int n, int k,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ scales, int kg) {
@@ -113,13 +132,13 @@ __global__ void __launch_bounds__(256) cast_128x128_kernel(const float* __restri
   if (lane == 0) wave_max[wave] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(wave_max[0], wave_max[1]), fmaxf(wave_max[2], wave_max[3]));
-  const float s = group_scale(amax);
+  const float s = group_scale<FMT>(amax);
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int row = nb * 128 + wave * 32 + 2 * i + (lane >> 5);
     if (row < n && col_ok)
       *reinterpret_cast<uint32_t*>(q + int64_t(row) * k + col) =
-          e4m3x4(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s), __fdiv_rn(v[i].z, s), __fdiv_rn(v[i].w, s));
+          fp8x4<FMT>(__fdiv_rn(v[i].x, s), __fdiv_rn(v[i].y, s), __fdiv_rn(v[i].z, s), __fdiv_rn(v[i].w, s));
   }
   if (threadIdx.x == 0) scales[int64_t(nb) * kg + g] = s;
 }

@@ -126,12 +126,17 @@ __device__ __forceinline__ void wait_coherent(v4f (&t)[8]) {
 }
 
 
+// FP8 formats of the operands (the f8f6f4 MFMA's per-operand format codes).
+constexpr int kFmtE4M3 = 0, kFmtE5M2 = 1;
+
 // One 16x16x128 FP8 x FP8 -> FP32 MFMA with zero accumulator input.  The
 // scaled gfx950 form is used with unit E8M0 scales (127 = 2^0), so it is the
-// plain product.  src0 supplies the output rows, src1 the output columns.
+// plain product.  src0 supplies the output rows, src1 the output columns;
+// F0 / F1 are their formats (E4M3 or E5M2).
+template <int F0 = kFmtE4M3, int F1 = kFmtE4M3>
 __device__ __forceinline__ v4f mfma16x16x128(const v8i& src0, const v8i& src1) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(src0, src1, zero, 0, 0, 0, 127, 0, 127);
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(src0, src1, zero, F0, F1, 0, 127, 0, 127);
 }
 
 }  // namespace fp8g

@@ -115,7 +115,7 @@ int env_int(const char* name, int fallback) {
   return (v && *v) ? std::atoi(v) : fallback;
 }
 
-DenseConfig dense_config(int m, int n, int k, bool allow_split) {
+DenseConfig dense_config(int m, int n, int k, bool allow_split, bool all_kinds = true) {
   DenseConfig c{};
   const int cus0 = effective_cus();
   // few 32-column tiles per CU: the K-group-sharing shapes; many: the plain ones
@@ -124,7 +124,7 @@ DenseConfig dense_config(int m, int n, int k, bool allow_split) {
   // large M but few 256 x 256 tiles: narrower tiles with split-K fill the CUs
   if (c.kind == kBig && cdiv(m, 256) * cdiv(n, 256) < cus0 / 2) c.kind = kS128N64;
   const int forced = env_int("FP8G_FORCE_CONFIG", -1);  // debugging and tuning only
-  if (forced >= 0 && forced < kKinds) c.kind = forced;
+  if (forced >= 0 && forced < kKinds && all_kinds) c.kind = forced;
   const KernelShape& ks = kShapes[c.kind];
   c.tiles_m = int(cdiv(m, ks.bm));
   c.tiles_n = int(cdiv(n, ks.bn));
@@ -163,29 +163,67 @@ unsigned next_epoch() {
   return e;
 }
 
-template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT, int KU = 1, int WK = 1>
+template <int BM, int BN, int WMW, int WNW, int ST, int MODE, bool SPLIT, int KU = 1, int WK = 1, int FMT = 0>
 void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT, KU, WK>), dim3(unsigned(grid)),
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, WMW, WNW, ST, MODE, SPLIT, KU, WK, FMT>), dim3(unsigned(grid)),
                      dim3(64 * WMW * WNW * WK), 0, s, p);
 }
 
-template <bool SPLIT>
+// FMT: bit 0 = LHS in E5M2, bit 1 = RHS in E5M2.  The E4M3 x E4M3 build has
+// every shape; the other format pairs have the shapes dense_config picks by
+// itself (a forced shape falls back to those).
+template <bool SPLIT, int FMT>
 void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+  if constexpr (FMT == 0) {
+    switch (kind) {
+      case kS64N64: launch_gemm<64, 64, 1, 4, 4, kDense, SPLIT>(p, grid, s); return;
+      case kS64N128: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); return;
+      case kS128N128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); return;
+      case kMid: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); return;
+      default: break;
+    }
+  }
   switch (kind) {
-    case kS64N64: launch_gemm<64, 64, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
-    case kS64N128: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); break;
-    case kS128N64: launch_gemm<128, 64, 2, 2, 4, kDense, SPLIT>(p, grid, s); break;
-    case kS128N128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
-    case kMid: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); break;
-    case kS64N32: launch_gemm<64, 32, 2, 2, 4, kDense, SPLIT>(p, grid, s); break;
-    case kS128N32: launch_gemm<128, 32, 4, 1, 4, kDense, SPLIT>(p, grid, s); break;
-    case kS64N32K4: launch_gemm<64, 32, 1, 1, 3, kDense, SPLIT, 4, 4>(p, grid, s); break;
-    case kS128N32K2: launch_gemm<128, 32, 2, 1, 3, kDense, SPLIT, 2, 2>(p, grid, s); break;
+    case kS128N64: launch_gemm<128, 64, 2, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
+    case kS64N32: launch_gemm<64, 32, 2, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
+    case kS128N32: launch_gemm<128, 32, 4, 1, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
+    case kS64N32K4: launch_gemm<64, 32, 1, 1, 3, kDense, SPLIT, 4, 4, FMT>(p, grid, s); break;
+    case kS128N32K2: launch_gemm<128, 32, 2, 1, 3, kDense, SPLIT, 2, 2, FMT>(p, grid, s); break;
     default:
       // the 256 x 256 tile cannot stage a split partial (dense_config never
       // asks for it)
-      if constexpr (!SPLIT) launch_gemm<256, 256, 4, 2, 2, kDense, false>(p, grid, s);
+      if constexpr (!SPLIT) launch_gemm<256, 256, 4, 2, 2, kDense, false, 1, 1, FMT>(p, grid, s);
       break;
+  }
+}
+
+template <bool SPLIT>
+void launch_dense_fmt(int fmt, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+  switch (fmt) {
+    case 1: launch_dense<SPLIT, 1>(kind, p, grid, s); break;
+    case 2: launch_dense<SPLIT, 2>(kind, p, grid, s); break;
+    case 3: launch_dense<SPLIT, 3>(kind, p, grid, s); break;
+    default: launch_dense<SPLIT, 0>(kind, p, grid, s); break;
+  }
+}
+
+template <int FMT>
+void launch_cast_1x128(const void* x, int x_dtype, bool pair, dim3 grid, hipStream_t s, int m, int k, uint8_t* q,
+                       float* scales, int64_t scales_ld) {
+  if (x_dtype == FP8G_F32) {
+    if (pair)
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<float, 2, FMT>), grid, dim3(256), 0, s,
+                         static_cast<const float*>(x), m, k, q, scales, scales_ld);
+    else
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<float, 1, FMT>), grid, dim3(256), 0, s,
+                         static_cast<const float*>(x), m, k, q, scales, scales_ld);
+  } else {
+    if (pair)
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<uint16_t, 2, FMT>), grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), m, k, q, scales, scales_ld);
+    else
+      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<uint16_t, 1, FMT>), grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(x), m, k, q, scales, scales_ld);
   }
 }
 
@@ -221,7 +259,17 @@ size_t fp8_gemm_workspace_bytes(int m, int n, int k, int num_groups) {
 int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
                 const uint8_t* rhs, const float* rhs_scales, uint16_t* out, int m, int n, int k,
                 void* workspace, size_t workspace_bytes, void* stream) {
+  return fp8_gemm_nt_fmt(lhs, FP8G_E4M3, lhs_scales, lhs_scales_ld, rhs, FP8G_E4M3, rhs_scales, out, m, n, k,
+                         workspace, workspace_bytes, stream);
+}
+
+int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales, int64_t lhs_scales_ld,
+                    const uint8_t* rhs, int rhs_format, const float* rhs_scales, uint16_t* out, int m, int n,
+                    int k, void* workspace, size_t workspace_bytes, void* stream) {
   if (m < 0) return FP8G_EINVAL;
+  if ((lhs_format != FP8G_E4M3 && lhs_format != FP8G_E5M2) || (rhs_format != FP8G_E4M3 && rhs_format != FP8G_E5M2))
+    return FP8G_EINVAL;
+  const int fmt = (lhs_format == FP8G_E5M2 ? 1 : 0) | (rhs_format == FP8G_E5M2 ? 2 : 0);
   if (int st = check_gemm_shape(n, k)) return st;
   if (m == 0 || n == 0) return FP8G_OK;
   if (!lhs || !lhs_scales || !rhs || !rhs_scales || !out) return FP8G_EINVAL;
@@ -230,8 +278,9 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
     return FP8G_EINVAL;
   if (int st = check_ld(lhs_scales_ld, m)) return st;
 
-  DenseConfig c = dense_config(m, n, k, true);
-  if (c.splits > 1 && (!workspace || workspace_bytes < dense_workspace(c, m, n))) c = dense_config(m, n, k, false);
+  DenseConfig c = dense_config(m, n, k, true, fmt == 0);
+  if (c.splits > 1 && (!workspace || workspace_bytes < dense_workspace(c, m, n)))
+    c = dense_config(m, n, k, false, fmt == 0);
 
   GemmParams p{};
   p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
@@ -249,10 +298,10 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
     std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
                  c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
   if (c.splits > 1) {
-    launch_dense<true>(c.kind, p, grid, s);
+    launch_dense_fmt<true>(fmt, c.kind, p, grid, s);
     return launched("gemm");
   }
-  launch_dense<false>(c.kind, p, grid, s);
+  launch_dense_fmt<false>(fmt, c.kind, p, grid, s);
   return launched("gemm");
 }
 
@@ -321,6 +370,12 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
 
 int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k, uint8_t* q, float* scales,
                              int64_t scales_ld, void* stream) {
+  return fp8_cast_per_token_group_fmt(x, x_dtype, FP8G_E4M3, m, k, q, scales, scales_ld, stream);
+}
+
+int fp8_cast_per_token_group_fmt(const void* x, int x_dtype, int q_format, int m, int k, uint8_t* q,
+                                 float* scales, int64_t scales_ld, void* stream) {
+  if (q_format != FP8G_E4M3 && q_format != FP8G_E5M2) return FP8G_EINVAL;
   if (m < 0 || k < 0) return FP8G_EINVAL;
   if (x_dtype != FP8G_F32 && x_dtype != FP8G_BF16) return FP8G_EINVAL;
   if (k % 8 != 0) return FP8G_EUNSUPPORTED;
@@ -335,25 +390,19 @@ int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k, uint8_t* 
   const bool pair = kg >= 64;
   const dim3 grid(unsigned(cdiv(m, 16)), unsigned(pair ? cdiv(kg, 2) : kg));
   auto s = static_cast<hipStream_t>(stream);
-  if (x_dtype == FP8G_F32) {
-    if (pair)
-      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<float, 2>), grid, dim3(256), 0, s, static_cast<const float*>(x), m,
-                         k, q, scales, scales_ld);
-    else
-      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<float, 1>), grid, dim3(256), 0, s, static_cast<const float*>(x), m,
-                         k, q, scales, scales_ld);
-  } else {
-    if (pair)
-      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<uint16_t, 2>), grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), m, k, q, scales, scales_ld);
-    else
-      hipLaunchKernelGGL((fp8g::cast_1x128_kernel<uint16_t, 1>), grid, dim3(256), 0, s,
-                         static_cast<const uint16_t*>(x), m, k, q, scales, scales_ld);
-  }
+  if (q_format == FP8G_E5M2)
+    launch_cast_1x128<fp8g::kFmtE5M2>(x, x_dtype, pair, grid, s, m, k, q, scales, scales_ld);
+  else
+    launch_cast_1x128<fp8g::kFmtE4M3>(x, x_dtype, pair, grid, s, m, k, q, scales, scales_ld);
   return launched("per-token-group cast");
 }
 
 int fp8_cast_per_block(const float* w, int n, int k, uint8_t* q, float* scales, void* stream) {
+  return fp8_cast_per_block_fmt(w, FP8G_E4M3, n, k, q, scales, stream);
+}
+
+int fp8_cast_per_block_fmt(const float* w, int q_format, int n, int k, uint8_t* q, float* scales, void* stream) {
+  if (q_format != FP8G_E4M3 && q_format != FP8G_E5M2) return FP8G_EINVAL;
   if (n < 0 || k < 0) return FP8G_EINVAL;
   if (k % 4 != 0) return FP8G_EUNSUPPORTED;
   if (n == 0 || k == 0) return FP8G_OK;
@@ -361,8 +410,12 @@ int fp8_cast_per_block(const float* w, int n, int k, uint8_t* q, float* scales, 
   if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FP8G_EINVAL;
   const int64_t kg = cdiv(k, 128), nb = cdiv(n, 128);
   if (kg > 65535 || nb > 0x7fffffff) return FP8G_EUNSUPPORTED;
-  hipLaunchKernelGGL(fp8g::cast_128x128_kernel, dim3(unsigned(nb), unsigned(kg)), dim3(256), 0,
-                     static_cast<hipStream_t>(stream), w, n, k, q, scales, int(kg));
+  if (q_format == FP8G_E5M2)
+    hipLaunchKernelGGL(fp8g::cast_128x128_kernel<fp8g::kFmtE5M2>, dim3(unsigned(nb), unsigned(kg)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), w, n, k, q, scales, int(kg));
+  else
+    hipLaunchKernelGGL(fp8g::cast_128x128_kernel<fp8g::kFmtE4M3>, dim3(unsigned(nb), unsigned(kg)), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), w, n, k, q, scales, int(kg));
   return launched("block cast");
 }
 

@@ -98,13 +98,15 @@ struct FragPtrs {
   const float* s;
 };
 
-// One K group of a wave's TN x TM sub-tiles, read from ring slot SLOT.  The
+// One K group of a wave's TN x TM sub-tiles, read from ring slot SLOT
+// (FMT: bit 0 set = the LHS holds E5M2 codes, bit 1 = the RHS does).  The
 // operand with fewer fragments is held in registers, the other is streamed
 // one fragment ahead.  Each MFMA is issued before the promotion of the
 // previous product, so the promotion FMAs run while the next MFMA occupies
 // the matrix core.
-template <int TM, int TN, int A_SLOT, int B_SLOT, int S_SLOT>
+template <int TM, int TN, int A_SLOT, int B_SLOT, int S_SLOT, int FMT = 0>
 __device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs& f, float sbv) {
+  constexpr int FB = (FMT >> 1) & 1, FA = FMT & 1;  // src0 = RHS fragment, src1 = LHS fragment
   constexpr int FRAG = 16 * kRowBytes;
   auto afrag = [&](int j) { return lds_frag(f.a0 + A_SLOT + j * FRAG, f.a1 + A_SLOT + j * FRAG); };
   auto bfrag = [&](int i) { return lds_frag(f.b0 + B_SLOT + i * FRAG, f.b1 + B_SLOT + i * FRAG); };
@@ -127,7 +129,7 @@ __device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs
       }
 #pragma unroll
       for (int i = 0; i < TN; ++i) {
-        const v4f pr = mfma16x16x128(bf[i], a_cur);
+        const v4f pr = mfma16x16x128<FB, FA>(bf[i], a_cur);
         const int t = j * TN + i;
         if (t > 0) promote(acc[(t - 1) % TN][(t - 1) / TN], prev, prev_s);
         prev = pr;
@@ -153,7 +155,7 @@ __device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs
       if (i + 1 < TN) b_next = bfrag(i + 1);
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
-        const v4f pr = mfma16x16x128(b_cur, af[j]);
+        const v4f pr = mfma16x16x128<FB, FA>(b_cur, af[j]);
         const int t = i * TM + j;
         if (t > 0) promote(acc[(t - 1) / TM][(t - 1) % TM], prev, sc[(t - 1) % TM]);
         prev = pr;
@@ -265,7 +267,9 @@ __device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int
 // cover the fixed latency of a stage's synchronisation and LDS reads; giving
 // each wave its own groups of a larger sub-tile keeps several independent
 // chains of MFMAs in flight.
-template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT, int KU = 1, int WK = 1>
+// FMT selects the operand formats (bit 0: LHS E5M2, bit 1: RHS E5M2).
+template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT, int KU = 1, int WK = 1,
+          int FMT = 0>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(const GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N * WK;  // 4 waves: one per SIMD; 8 waves: two per SIMD
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
@@ -458,7 +462,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
         constexpr int slot = stage * KU + decltype(uc)::value * WK;  // + wk, folded into f
         const int gl = KU * it + decltype(uc)::value * WK + wk;
         if (KU == 1 || gl < ngroups)
-          group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES>(acc, f, sb_row[gl]);
+          group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES, FMT>(acc, f, sb_row[gl]);
       });
   };
   for (int it = 0; it < niter; it += STAGES) {

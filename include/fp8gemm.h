@@ -57,6 +57,12 @@ enum {
 /* Element type of the cast helper's input. */
 enum { FP8G_F32 = 0, FP8G_BF16 = 1 };
 
+/* FP8 formats ("DeepGEMM: FP8 GEMM kernel optimisation practice on Hopper
+ * Tensor Cores", sections 1.3 and 3.1: A and B in E4M3 or E5M2).  OCP E4M3FN
+ * (max 448, no infinities) and OCP E5M2 (max 57344).  The entry points
+ * without a format argument use E4M3. */
+enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 };
+
 /* Dense NT GEMM: out[m][n] = bf16( sum_k dec(lhs[i][t]) * sa(i, t/128)
  *                                        * dec(rhs[j][t]) * sb(j/128, t/128) ),
  * evaluated with one FP32 promotion per 128-wide K group.
@@ -79,6 +85,14 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
                 const uint8_t* rhs, const float* rhs_scales,
                 uint16_t* out, int m, int n, int k,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp8_gemm_nt with each operand's format given: lhs_format / rhs_format are
+ * FP8G_E4M3 or FP8G_E5M2, in any combination (FP8G_EINVAL otherwise).  The
+ * arithmetic is the same; only the decoding of the codes changes. */
+int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales, int64_t lhs_scales_ld,
+                    const uint8_t* rhs, int rhs_format, const float* rhs_scales,
+                    uint16_t* out, int m, int n, int k,
+                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* Contiguous-layout grouped GEMM (MoE prefill / training forward).
  *   lhs        [m_total][k];  lhs_scales [KG][lhs_scales_ld >= m_total]
@@ -125,12 +139,21 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
 int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
                              uint8_t* q, float* scales, int64_t scales_ld, void* stream);
 
+/* The per-token-group cast to either format: q_format FP8G_E4M3 (scale =
+ * amax / 448) or FP8G_E5M2 (scale = amax / 57344, q = E5M2(x / scale),
+ * round-to-nearest-even, saturating at +-57344). */
+int fp8_cast_per_token_group_fmt(const void* x, int x_dtype, int q_format, int m, int k,
+                                 uint8_t* q, float* scales, int64_t scales_ld, void* stream);
+
 /* 128 x 128 block cast for weights (the RHS scale granularity of the
  * "Basic usage" example): one scale per block, computed as above over the
  * block's real elements (edge blocks may be partial).
  *   w       [n][k] FP32;  q [n][k] E4M3 codes;  scales [NB][KG] FP32 */
 int fp8_cast_per_block(const float* w, int n, int k,
                        uint8_t* q, float* scales, void* stream);
+/* The same to either format (q_format as for fp8_cast_per_token_group_fmt). */
+int fp8_cast_per_block_fmt(const float* w, int q_format, int n, int k,
+                           uint8_t* q, float* scales, void* stream);
 
 /* ---- MoE layout steps around the grouped GEMMs -----------------------------
  * The flow of the kwkr.cn DeepGEMM usage article (section 3.2; section 4.3:

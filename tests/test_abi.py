@@ -65,6 +65,26 @@ def test_host_validation_paths(lib):
     assert b(None, 4, 6, None, None, None) == binding.FP8G_EUNSUPPORTED
 
 
+def test_format_entry_points_validate(lib):
+    E4, E5 = binding.FP8G_E4M3, binding.FP8G_E5M2
+    g = lib.fp8_gemm_nt_fmt
+    for fa, fb in ((2, E4), (E4, -1), (E5, 7)):
+        assert g(None, fa, None, 4, None, fb, None, None, 4, 8, 128, None, 0, None) == binding.FP8G_EINVAL
+    for fa, fb in ((E4, E4), (E5, E4), (E4, E5), (E5, E5)):
+        # the same size checks as the E4M3 entry point, and empty problems are no-ops
+        assert g(None, fa, None, 4, None, fb, None, None, 4, 8, 100, None, 0, None) == binding.FP8G_EUNSUPPORTED
+        assert g(None, fa, None, 4, None, fb, None, None, 0, 8, 128, None, 0, None) == binding.FP8G_OK
+    t = lib.fp8_cast_per_token_group_fmt
+    assert t(None, 0, 3, 0, 128, None, None, 4, None) == binding.FP8G_EINVAL
+    assert t(None, 0, E5, 4, 128, None, None, 4, None) == binding.FP8G_EINVAL
+    assert t(None, 0, E5, 4, 12, None, None, 4, None) == binding.FP8G_EUNSUPPORTED
+    b = lib.fp8_cast_per_block_fmt
+    assert b(None, 2, 0, 128, None, None, None) == binding.FP8G_EINVAL
+    assert b(None, E5, 4, 6, None, None, None) == binding.FP8G_EUNSUPPORTED
+    with pytest.raises(ValueError):
+        binding._fmt(2, "q_format")
+
+
 def test_cu_limit_setter(lib):
     prev = binding.fp8_set_num_cus(17)
     try:

@@ -8,7 +8,7 @@ seeded synthetic inputs used by the tests and the benchmark.
 from .binding import (  # noqa: F401
     FP8G_BF16, FP8G_E4M3, FP8G_E5M2, FP8G_EINVAL, FP8G_ELAUNCH, FP8G_EUNSUPPORTED, FP8G_F32, FP8G_OK,
     Fp8GemmError, fp8_cast_per_block, fp8_cast_per_block_fmt, fp8_cast_per_token_group,
-    fp8_cast_per_token_group_fmt, fp8_gemm_nt, fp8_gemm_nt_fmt,
+    fp8_cast_per_token_group_fmt, fp8_gemm_describe, fp8_gemm_nt, fp8_gemm_nt_fmt,
     fp8_gemm_workspace_bytes, fp8_get_num_cus, fp8_grouped_gemm_contiguous,
     fp8_grouped_gemm_masked, fp8_set_num_cus, fp8_status_string,
     fp8_moe_contiguous_rows, fp8_moe_gather_rows, fp8_moe_layout_contiguous, fp8_moe_layout_masked,

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "fp8_grouped_gemm_masked": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "fp8_cast_per_token_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
     "fp8_cast_per_block": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
+    "fp8_gemm_describe": ([_i32, _i32, _i32, ctypes.c_char_p, _sz], _i32),
     "fp8_gemm_nt_fmt": ([_vp, _i32, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "fp8_cast_per_token_group_fmt": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
     "fp8_cast_per_block_fmt": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
@@ -258,6 +259,15 @@ def fp8_cast_per_block(w, q, scales, stream=None):
 
 def fp8_gemm_workspace_bytes(m, n, k, num_groups=1) -> int:
     return int(lib().fp8_gemm_workspace_bytes(int(m), int(n), int(k), int(num_groups)))
+
+
+def fp8_gemm_describe(m: int, n: int, k: int) -> str:
+    """The dense configuration fp8_gemm_nt picks for (m, n, k), as text
+    (host only; launches nothing)."""
+    buf = ctypes.create_string_buffer(256)
+    st = lib().fp8_gemm_describe(m, n, k, buf, len(buf))
+    _check("fp8_gemm_describe", st)
+    return buf.value.decode()
 
 
 def fp8_set_num_cus(num_cus: int) -> int:

@@ -256,6 +256,20 @@ size_t fp8_gemm_workspace_bytes(int m, int n, int k, int num_groups) {
   return dense_workspace(c, m, n);
 }
 
+int fp8_gemm_describe(int m, int n, int k, char* buf, size_t len) {
+  if (!buf || len == 0 || m < 0) return FP8G_EINVAL;
+  if (const int st = check_gemm_shape(n, k)) return st;
+  if (m == 0 || n == 0) {
+    std::snprintf(buf, len, "empty");
+    return FP8G_OK;
+  }
+  const DenseConfig c = dense_config(m, n, k, true);
+  const KernelShape& ks = kShapes[c.kind];
+  std::snprintf(buf, len, "tile=%dx%d waves=%d stages=%d ku=%d splits=%d grid=%lld", ks.bm, ks.bn, ks.waves,
+                ks.stages, ks.ku, c.splits, (long long)(int64_t(c.tiles_m) * c.tiles_n * c.splits));
+  return FP8G_OK;
+}
+
 int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
                 const uint8_t* rhs, const float* rhs_scales, uint16_t* out, int m, int n, int k,
                 void* workspace, size_t workspace_bytes, void* stream) {

@@ -86,6 +86,15 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
                 uint16_t* out, int m, int n, int k,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Host only, launches nothing: writes a one-line description of the dense
+ * configuration fp8_gemm_nt picks for (m, n, k) when the split-K workspace
+ * is large enough ("tile=BMxBN waves=W stages=S ku=U splits=P grid=G", or
+ * "empty"), NUL-terminated and truncated to len bytes.  The counterpart of
+ * the JIT debug output in "DeepSeek open-source week, day 3: DeepGEMM"
+ * (environment variables).  FP8G_EINVAL for a null buffer or negative m;
+ * FP8G_EUNSUPPORTED for n, k fp8_gemm_nt rejects. */
+int fp8_gemm_describe(int m, int n, int k, char* buf, size_t len);
+
 /* fp8_gemm_nt with each operand's format given: lhs_format / rhs_format are
  * FP8G_E4M3 or FP8G_E5M2, in any combination (FP8G_EINVAL otherwise).  The
  * arithmetic is the same; only the decoding of the codes changes. */

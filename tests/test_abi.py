@@ -65,6 +65,27 @@ def test_host_validation_paths(lib):
     assert b(None, 4, 6, None, None, None) == binding.FP8G_EUNSUPPORTED
 
 
+def test_describe_reports_the_tile_choice(lib):
+    """Host-only tile choice for a 256-CU device: 256 x 256 tiles for large
+    M, narrow split tiles for small M."""
+    if binding.fp8_get_num_cus() != 256:
+        pytest.skip("the expectations are for a 256-CU device (or no device)")
+    d = binding.fp8_gemm_describe
+    for shape in [(4096, 7168, 16384), (4096, 4096, 7168), (4096, 24576, 1536), (8192, 8192, 8192)]:
+        assert d(*shape).startswith("tile=256x256 "), shape
+    assert "splits=1 grid=448" in d(4096, 7168, 16384)
+    small = d(64, 2112, 7168)
+    assert small.startswith("tile=64x32 ") and "splits=1" not in small
+    assert d(0, 8, 128) == "empty"
+    with pytest.raises(binding.Fp8GemmError):
+        d(4, 8, 100)
+    buf = ctypes.create_string_buffer(8)
+    assert lib.fp8_gemm_describe(4096, 7168, 16384, buf, 8) == binding.FP8G_OK
+    assert buf.value == b"tile=25"        # truncated, NUL-terminated
+    assert lib.fp8_gemm_describe(4, 8, 128, None, 8) == binding.FP8G_EINVAL
+    assert lib.fp8_gemm_describe(-1, 8, 128, buf, 8) == binding.FP8G_EINVAL
+
+
 def test_format_entry_points_validate(lib):
     E4, E5 = binding.FP8G_E4M3, binding.FP8G_E5M2
     g = lib.fp8_gemm_nt_fmt

@@ -13,4 +13,8 @@ from .binding import (  # noqa: F401
     fp8_grouped_gemm_masked, fp8_set_num_cus, fp8_status_string,
     fp8_moe_contiguous_rows, fp8_moe_gather_rows, fp8_moe_layout_contiguous, fp8_moe_layout_masked,
     fp8_moe_layout_workspace_bytes, fp8_moe_scatter_rows,
+    FP8G_JIT_CONTIGUOUS, FP8G_JIT_DENSE, FP8G_JIT_MASKED, Fp8GemmConfig, fp8_jit_config_supported,
+    fp8_jit_default_config, fp8_jit_gemm_nt, fp8_jit_gemm_workspace_bytes, fp8_jit_get_cache_dir,
+    fp8_jit_grouped_gemm_contiguous, fp8_jit_grouped_gemm_masked, fp8_jit_set_cache_dir, fp8_jit_stats,
+    fp8_jit_warmup,
 )

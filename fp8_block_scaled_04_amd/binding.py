@@ -26,9 +26,25 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "fp8gemm.h")
 FP8G_OK, FP8G_EINVAL, FP8G_EUNSUPPORTED, FP8G_ELAUNCH = 0, -1, -2, -3
 FP8G_F32, FP8G_BF16 = 0, 1
 FP8G_E4M3, FP8G_E5M2 = 0, 1
+FP8G_JIT_DENSE, FP8G_JIT_CONTIGUOUS, FP8G_JIT_MASKED = 0, 1, 2
 
 _lib = None
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+
+
+class Fp8GemmConfig(ctypes.Structure):
+    """fp8_gemm_config: the tile configuration of a runtime-specialised GEMM."""
+    _fields_ = [(f, ctypes.c_int) for f in ("block_m", "block_n", "waves_m", "waves_n", "waves_k", "stages",
+                                          "k_per_stage", "splits", "specialize")]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+    def __repr__(self):
+        return f"Fp8GemmConfig({self.as_dict()})"
+
+
+_cfgp = ctypes.POINTER(Fp8GemmConfig)
 
 _SIGNATURES = {
     "fp8_gemm_nt": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
@@ -44,6 +60,17 @@ _SIGNATURES = {
     "fp8_set_num_cus": ([_i32], _i32),
     "fp8_get_num_cus": ([], _i32),
     "fp8_status_string": ([_i32], ctypes.c_char_p),
+    "fp8_jit_default_config": ([_i32, _i32, _i32, _i32, _cfgp], _i32),
+    "fp8_jit_config_supported": ([_i32, _cfgp], _i32),
+    "fp8_jit_warmup": ([_i32, _i32, _i32, _i32, _i32, _cfgp], _i32),
+    "fp8_jit_gemm_workspace_bytes": ([_i32, _i32, _i32, _cfgp], _sz),
+    "fp8_jit_gemm_nt": ([_vp, _i32, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _cfgp, _vp, _sz, _vp], _i32),
+    "fp8_jit_grouped_gemm_contiguous": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _cfgp, _vp],
+                                        _i32),
+    "fp8_jit_grouped_gemm_masked": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _cfgp, _vp], _i32),
+    "fp8_jit_set_cache_dir": ([ctypes.c_char_p], _i32),
+    "fp8_jit_get_cache_dir": ([ctypes.c_char_p, _sz], _i32),
+    "fp8_jit_stats": ([ctypes.POINTER(ctypes.c_longlong), _i32], _i32),
     "fp8_moe_contiguous_rows": ([_i32, _i32], _i32),
     "fp8_moe_layout_workspace_bytes": ([_i32, _i32], _sz),
     "fp8_moe_layout_contiguous": ([_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp], _i32),
@@ -173,6 +200,112 @@ def fp8_gemm_nt_fmt(lhs, lhs_format, lhs_scales, rhs, rhs_format, rhs_scales, ou
                                _p(rhs_scales), _p(out), m, n, k, _p(workspace), ws_bytes, _stream(stream))
     _check("fp8_gemm_nt_fmt", st)
     return out
+
+
+# ---- runtime shape specialisation ---------------------------------------------
+def _config(config, **overrides):
+    """An Fp8GemmConfig from None (keep None), a config, or a dict of fields;
+    keyword overrides replace fields."""
+    if config is None and not overrides:
+        return None
+    c = Fp8GemmConfig()
+    if isinstance(config, Fp8GemmConfig):
+        ctypes.pointer(c)[0] = config
+    elif isinstance(config, dict):
+        for f, v in config.items():
+            setattr(c, f, int(v))
+    elif config is not None:
+        raise TypeError("config must be an Fp8GemmConfig, a dict or None")
+    for f, v in overrides.items():
+        setattr(c, f, int(v))
+    return c
+
+
+def _cref(c):
+    return None if c is None else ctypes.byref(c)
+
+
+def fp8_jit_default_config(mode, m, n, k) -> Fp8GemmConfig:
+    """The configuration the ahead-of-time path uses for this shape."""
+    c = Fp8GemmConfig()
+    _check("fp8_jit_default_config", lib().fp8_jit_default_config(mode, m, n, k, ctypes.byref(c)))
+    return c
+
+
+def fp8_jit_config_supported(mode, config) -> bool:
+    return lib().fp8_jit_config_supported(mode, _cref(_config(config))) == FP8G_OK
+
+
+def fp8_jit_warmup(mode, n, k, lhs_format=FP8G_E4M3, rhs_format=FP8G_E4M3, config=None):
+    """Compile (or read from the cache) and load a kernel without launching it."""
+    _check("fp8_jit_warmup", lib().fp8_jit_warmup(mode, n, k, lhs_format, rhs_format, _cref(_config(config))))
+
+
+def fp8_jit_gemm_workspace_bytes(m, n, k, config) -> int:
+    return int(lib().fp8_jit_gemm_workspace_bytes(m, n, k, _cref(_config(config))))
+
+
+def fp8_jit_gemm_nt(lhs, lhs_format, lhs_scales, rhs, rhs_format, rhs_scales, out, config=None, workspace=None,
+                    stream=None):
+    """fp8_gemm_nt_fmt through a runtime-specialised kernel (config None:
+    the ahead-of-time choice)."""
+    lhs_format, rhs_format = _fmt(lhs_format, "lhs_format"), _fmt(rhs_format, "rhs_format")
+    lhs, rhs = _codes(lhs, "lhs", lhs_format), _codes(rhs, "rhs", rhs_format)
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out = _bf16(out, "out")
+    m, k = lhs.shape
+    n = rhs.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().fp8_jit_gemm_nt(_p(lhs), lhs_format, _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), rhs_format,
+                               _p(rhs_scales), _p(out), m, n, k, _cref(_config(config)), _p(workspace), ws_bytes,
+                               _stream(stream))
+    _check("fp8_jit_gemm_nt", st)
+    return out
+
+
+def fp8_jit_grouped_gemm_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices, config=None, stream=None):
+    lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out, m_indices = _bf16(out, "out"), _i32t(m_indices, "m_indices")
+    M, k = lhs.shape
+    G, n, _ = rhs.shape
+    st = lib().fp8_jit_grouped_gemm_contiguous(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs),
+                                               _p(rhs_scales), _p(out), _p(m_indices), M, n, k, G,
+                                               _cref(_config(config)), _stream(stream))
+    _check("fp8_jit_grouped_gemm_contiguous", st)
+    return out
+
+
+def fp8_jit_grouped_gemm_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m, config=None, stream=None):
+    lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out, masked_m = _bf16(out, "out"), _i32t(masked_m, "masked_m")
+    G, max_m, k = lhs.shape
+    n = rhs.shape[1]
+    st = lib().fp8_jit_grouped_gemm_masked(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales),
+                                           _p(out), _p(masked_m), G, max_m, n, k, _cref(_config(config)),
+                                           _stream(stream))
+    _check("fp8_jit_grouped_gemm_masked", st)
+    return out
+
+
+def fp8_jit_set_cache_dir(path=None):
+    _check("fp8_jit_set_cache_dir", lib().fp8_jit_set_cache_dir(None if path is None else str(path).encode()))
+
+
+def fp8_jit_get_cache_dir() -> str:
+    buf = ctypes.create_string_buffer(4096)
+    _check("fp8_jit_get_cache_dir", lib().fp8_jit_get_cache_dir(buf, len(buf)))
+    return buf.value.decode()
+
+
+JIT_STAT_NAMES = ("memory_hits", "disk_hits", "compiles", "rejected_files", "failed_compiles")
+
+
+def fp8_jit_stats() -> dict:
+    arr = (ctypes.c_longlong * len(JIT_STAT_NAMES))()
+    _check("fp8_jit_stats", lib().fp8_jit_stats(arr, len(arr)))
+    return dict(zip(JIT_STAT_NAMES, list(arr)))
 
 
 def fp8_grouped_gemm_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices, stream=None):

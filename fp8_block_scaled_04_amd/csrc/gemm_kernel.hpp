@@ -268,8 +268,10 @@ __device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int
 // each wave its own groups of a larger sub-tile keeps several independent
 // chains of MFMAs in flight.
 // FMT selects the operand formats (bit 0: LHS E5M2, bit 1: RHS E5M2).
+// NSPEC / KSPEC > 0 make n / k compile-time constants (the runtime
+// specialisation builds them per shape); 0 takes them from the parameters.
 template <int BM, int BN, int WAVES_M, int WAVES_N, int STAGES, int MODE, bool SPLIT, int KU = 1, int WK = 1,
-          int FMT = 0>
+          int FMT = 0, int NSPEC = 0, int KSPEC = 0>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(const GemmParams p) {
   constexpr int NW = WAVES_M * WAVES_N * WK;  // 4 waves: one per SIMD; 8 waves: two per SIMD
   static_assert(NW == 4 || NW == 8, "four or eight waves per workgroup");
@@ -294,6 +296,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[RING];
   __shared__ float sb_cache[SB_BLOCKS][kMaxGroups];
+
+  static_assert(NSPEC >= 0 && NSPEC % 8 == 0 && KSPEC >= 0 && KSPEC % kGroupK == 0 &&
+                KSPEC <= kGroupK * kMaxGroups, "specialised shape");
+  const int shape_n = NSPEC > 0 ? NSPEC : p.n;
+  const int shape_k = KSPEC > 0 ? KSPEC : p.k;
+  const int shape_kg = KSPEC > 0 ? KSPEC / kGroupK : p.kg;
+  const int shape_nb = NSPEC > 0 ? (NSPEC + 127) / 128 : p.nb;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = uniform(threadIdx.x >> 6);
@@ -351,21 +360,21 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     contiguous_locate(cs, p.m_indices, p.m / 128, m_tile, block, nblocks, gi);
     m0 = 128 * block;
     rows = m0 + 128 * nblocks;  // rows of other blocks are neither used nor written
-    B += int64_t(gi) * p.n * p.k;
-    SB += int64_t(gi) * p.nb * p.kg;
+    B += int64_t(gi) * shape_n * shape_k;
+    SB += int64_t(gi) * shape_nb * shape_kg;
   } else if constexpr (MODE == kMasked) {
     rows = min(max(p.masked_m[group], 0), p.m);
     if (m0 >= rows) return;  // nothing valid in this tile
-    A += int64_t(group) * p.m * p.k;
-    SA += int64_t(group) * p.kg * p.sa_ld;
-    B += int64_t(group) * p.n * p.k;
-    SB += int64_t(group) * p.nb * p.kg;
-    OUT += int64_t(group) * p.m * p.n;
+    A += int64_t(group) * p.m * shape_k;
+    SA += int64_t(group) * shape_kg * p.sa_ld;
+    B += int64_t(group) * shape_n * shape_k;
+    SB += int64_t(group) * shape_nb * shape_kg;
+    OUT += int64_t(group) * p.m * shape_n;
   }
-  int g_begin = 0, g_end = p.kg;
+  int g_begin = 0, g_end = shape_kg;
   if constexpr (SPLIT) {
     g_begin = split * p.groups_per_split;
-    g_end = min(p.kg, g_begin + p.groups_per_split);
+    g_end = min(shape_kg, g_begin + p.groups_per_split);
   }
   const int ngroups = g_end - g_begin;
   const int niter = (ngroups + KU - 1) / KU;  // ring stages
@@ -379,13 +388,13 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   for (int i = 0; i < A_COPIES; ++i) {
     const int u = i * NW + wave;
     const int r = 16 * (u >> 1) + tile_row(u & 1, lane);
-    a_off[i] = uint32_t(min(m0 + r, rows - 1)) * uint32_t(p.k) + 16u * tile_chunk(u & 1, lane);
+    a_off[i] = uint32_t(min(m0 + r, rows - 1)) * uint32_t(shape_k) + 16u * tile_chunk(u & 1, lane);
   }
 #pragma unroll
   for (int i = 0; i < B_COPIES; ++i) {
     const int u = i * NW + wave;
     const int r = 16 * (u >> 1) + tile_row(u & 1, lane);
-    b_off[i] = uint32_t(min(n0 + r, p.n - 1)) * uint32_t(p.k) + 16u * tile_chunk(u & 1, lane);
+    b_off[i] = uint32_t(min(n0 + r, shape_n - 1)) * uint32_t(shape_k) + 16u * tile_chunk(u & 1, lane);
   }
   const uint32_t s_off = 4u * uint32_t(min(m0 + 4 * lane, int(p.sa_ld) - 4));
   const uint32_t lds0 = uniform(int(lds_addr(smem)));
@@ -424,9 +433,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     const uint32_t sb_lds = uniform(int(lds_addr(&sb_cache[0][0])));
     for (int c = wave; c < SB_BLOCKS * ((ngroups + 63) / 64); c += NW) {
       const int b = c % SB_BLOCKS, part = c / SB_BLOCKS;
-      const int blk = min(n0 / 128 + b, p.nb - 1);
+      const int blk = min(n0 / 128 + b, shape_nb - 1);
       const int g = min(g_begin + 64 * part + lane, g_end - 1);
-      copy4_to_lds(SB + int64_t(blk) * p.kg, 4u * uint32_t(g), sb_lds + 4 * (b * kMaxGroups + 64 * part));
+      copy4_to_lds(SB + int64_t(blk) * shape_kg, 4u * uint32_t(g), sb_lds + 4 * (b * kMaxGroups + 64 * part));
     }
   }
   const float* sb_row = sb_cache[wrow_n / 128];
@@ -465,6 +474,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
           group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES, FMT>(acc, f, sb_row[gl]);
       });
   };
+  // Kept rolled: with k a compile-time constant the compiler would unroll
+  // the whole K loop, run out of registers and spill, and spill traffic
+  // would share the vector-memory counter the ring waits count copies with.
+#pragma clang loop unroll(disable)
   for (int it = 0; it < niter; it += STAGES) {
     static_for<0, STAGES>([&](auto ic) __attribute__((always_inline)) {
       constexpr int I = decltype(ic)::value;
@@ -520,11 +533,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
               acc[i][j];
     }
     __syncthreads();
-    const int64_t mn = int64_t(p.m) * p.n;
+    const int64_t mn = int64_t(p.m) * shape_n;
     for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
       const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
-      if (m0 + r < rows && n0 + c4 < p.n)
-        store16_coherent(p.partial + split * mn + int64_t(m0 + r) * p.n + n0 + c4,
+      if (m0 + r < rows && n0 + c4 < shape_n)
+        store16_coherent(p.partial + split * mn + int64_t(m0 + r) * shape_n + n0 + c4,
                          *reinterpret_cast<const v4f*>(stage + r * LDT + c4));
     }
     __shared__ int last_arrival;
@@ -549,8 +562,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     // all splits of a chunk are requested before one wait (kMaxSplits <= 8)
     for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
       const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
-      if (m0 + r < rows && n0 + c4 < p.n) {
-        const float* P = p.partial + int64_t(m0 + r) * p.n + n0 + c4;
+      if (m0 + r < rows && n0 + c4 < shape_n) {
+        const float* P = p.partial + int64_t(m0 + r) * shape_n + n0 + c4;
         const v4f mine = *reinterpret_cast<const v4f*>(stage + r * LDT + c4);
         v4f t[8];
 #pragma unroll
@@ -564,7 +577,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
         uint2 v;
         v.x = pack_bf16x2(sum[0], sum[1]);
         v.y = pack_bf16x2(sum[2], sum[3]);
-        *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * p.n + n0 + c4) = v;
+        *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * shape_n + n0 + c4) = v;
       }
     }
   } else {
@@ -575,11 +588,11 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
 #pragma unroll
       for (int j = 0; j < TM; ++j) {
         const int tok = m0 + wrow_m + 16 * j + (lane & 15);
-        if (tok < rows && col < p.n) {
+        if (tok < rows && col < shape_n) {
           uint2 v;
           v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
           v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-          *reinterpret_cast<uint2*>(OUT + int64_t(tok) * p.n + col) = v;
+          *reinterpret_cast<uint2*>(OUT + int64_t(tok) * shape_n + col) = v;
         }
       }
     }

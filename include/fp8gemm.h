@@ -148,6 +148,73 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
 int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
                              uint8_t* q, float* scales, int64_t scales_ld, void* stream);
 
+/* ---- Runtime shape specialisation -------------------------------------------
+ * ("DeepSeek open-source week, day 3: DeepGEMM", "Core features": kernels
+ * compiled at run time per shape; its environment-variable list: a cache
+ * directory and JIT debug output; the kwkr.cn usage article, sections 2.3
+ * and 3.3: per-shape compilation, a warm-up, a cache kept across restarts.)
+ *
+ * The fp8_jit_* GEMMs take the same arguments as the entry points above plus
+ * a tile configuration (NULL: the one the ahead-of-time path would use).
+ * The kernel for (configuration, operand formats, target, and n and k when
+ * `specialize` is set) is compiled with hipRTC on first use, with the
+ * device code-generation options of the library build, kept on disk in the
+ * cache directory (default $FP8G_CACHE_DIR, else $HOME/.cache/fp8gemm) and
+ * loaded once per device per process.  A cache file that does not match its
+ * key, size or checksum is ignored, counted and replaced.  The first call
+ * for a configuration therefore compiles (about a second) or reads the
+ * disk; later calls only launch.  FP8G_JIT_DEBUG=1 reports compilations and
+ * cache use on stderr.  Results equal the ahead-of-time kernels' for the
+ * same configuration. */
+enum { FP8G_JIT_DENSE = 0, FP8G_JIT_CONTIGUOUS = 1, FP8G_JIT_MASKED = 2 };
+
+typedef struct fp8_gemm_config {
+  int block_m;      /* tile rows (tokens), <= 256, a multiple of 8 * waves */
+  int block_n;      /* tile columns (outputs), <= 256, a multiple of 8 * waves */
+  int waves_m;      /* wave grid over the tile: waves_m * waves_n * waves_k is 4 or 8; */
+  int waves_n;      /*   each wave's share is a multiple of 16 by 16, at most 32 MFMA */
+  int waves_k;      /*   tiles, and its n range divides 128 */
+  int stages;       /* LDS ring stages, 2..8 */
+  int k_per_stage;  /* 128-wide K groups per stage, 1..4, a multiple of waves_k */
+  int splits;       /* split-K workgroups per tile, 1..8 (dense only; grouped: 1) */
+  int specialize;   /* nonzero: n and k are compiled in */
+} fp8_gemm_config;
+
+/* The configuration the ahead-of-time path uses for `mode` (FP8G_JIT_*) and
+ * this shape. */
+int fp8_jit_default_config(int mode, int m, int n, int k, fp8_gemm_config* config);
+/* FP8G_OK if `config` can be built for `mode`, FP8G_EUNSUPPORTED if not
+ * (limits listed in fp8_gemm_config; LDS use <= 160 KB). */
+int fp8_jit_config_supported(int mode, const fp8_gemm_config* config);
+/* Compiles (or finds in the cache) and loads the kernel for a shape without
+ * launching it: the warm-up before timing.  Without a device it only fills
+ * the disk cache. */
+int fp8_jit_warmup(int mode, int n, int k, int lhs_format, int rhs_format, const fp8_gemm_config* config);
+/* Split-K workspace of fp8_jit_gemm_nt for this configuration (0 if none). */
+size_t fp8_jit_gemm_workspace_bytes(int m, int n, int k, const fp8_gemm_config* config);
+int fp8_jit_gemm_nt(const uint8_t* lhs, int lhs_format, const float* lhs_scales, int64_t lhs_scales_ld,
+                    const uint8_t* rhs, int rhs_format, const float* rhs_scales,
+                    uint16_t* out, int m, int n, int k, const fp8_gemm_config* config,
+                    void* workspace, size_t workspace_bytes, void* stream);
+/* config->block_m must be 256 (tiles are one or two 128-row blocks). */
+int fp8_jit_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                                    const uint8_t* rhs, const float* rhs_scales,
+                                    uint16_t* out, const int32_t* m_indices,
+                                    int m_total, int n, int k, int num_groups,
+                                    const fp8_gemm_config* config, void* stream);
+int fp8_jit_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                                const uint8_t* rhs, const float* rhs_scales,
+                                uint16_t* out, const int32_t* masked_m,
+                                int num_groups, int max_m, int n, int k,
+                                const fp8_gemm_config* config, void* stream);
+/* Cache directory for later compilations (NULL or "": the default). */
+int fp8_jit_set_cache_dir(const char* dir);
+int fp8_jit_get_cache_dir(char* buf, size_t len);
+/* Up to 5 counters since the library was loaded: kernels found loaded in
+ * memory, read from the disk cache, compiled, cache files rejected,
+ * compilations that failed. */
+int fp8_jit_stats(long long* counts, int n);
+
 /* The per-token-group cast to either format: q_format FP8G_E4M3 (scale =
  * amax / 448) or FP8G_E5M2 (scale = amax / 57344, q = E5M2(x / scale),
  * round-to-nearest-even, saturating at +-57344). */

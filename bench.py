@@ -83,6 +83,7 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="run only a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--digest", action="store_true", help="print the GEMM kernel source digest and exit")
+    ap.add_argument("--no-jit", action="store_true", help="skip the runtime-specialised kernels' timings")
     ap.add_argument("--no-grouped", action="store_true",
                     help="skip the grouped-GEMM measurements (MoE prefill and decode configurations)")
     args = ap.parse_args()
@@ -258,6 +259,8 @@ def main():
         "by_shape": by_shape,
     }
 
+    if not args.no_jit:
+        result["jit"] = jit_measurements(torch, stream, cases)
     if not args.no_grouped and not args.shape:
         del cases, sets
         torch.cuda.empty_cache()
@@ -265,6 +268,38 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def jit_measurements(torch, stream, cases):
+    """Runtime shape specialisation per sweep shape: the ahead-of-time tile
+    configuration rebuilt with n and k compiled in (compile time on a cold
+    cache, then timed like the ahead-of-time kernel)."""
+    from fp8_block_scaled_04_amd import binding
+
+    out = []
+    for c in cases:
+        m, n, k = c["m"], c["n"], c["k"]
+        cfg = binding._config(binding.fp8_jit_default_config(binding.FP8G_JIT_DENSE, m, n, k), specialize=1)
+        t0 = time.perf_counter()
+        try:
+            binding.fp8_jit_warmup(binding.FP8G_JIT_DENSE, n, k, config=cfg)
+        except binding.Fp8GemmError as e:   # e.g. the build would spill registers: refused
+            out.append(dict(m=m, n=n, k=k, refused=binding.status_string(e.status)))
+            continue
+        compile_s = time.perf_counter() - t0
+
+        def jit(b, st, c=c, cfg=cfg):
+            binding.fp8_jit_gemm_nt(b["q"], binding.FP8G_E4M3, b["s"], b["qb"], binding.FP8G_E4M3, b["sb"], b["out"],
+                                    config=cfg, workspace=c["ws"], stream=st)
+
+        reps = max(10, min(200, int(2e4 / max(1.0, c["flop"] / 1e9))))
+        ms = float(np.median(replay_mean_ms(torch, stream, jit, c["sets"], reps, 3)))
+        out.append(dict(m=m, n=n, k=k, jit_us=round(ms * 1e3, 2), aot_us=round(c["gemm_ms"] * 1e3, 2),
+                        aot_over_jit=round(c["gemm_ms"] / ms, 3), first_call_s=round(compile_s, 2)))
+        print(f"[bench] jit {m}x{n}x{k}: {ms * 1e3:.2f} us (ahead of time {c['gemm_ms'] * 1e3:.2f} us)",
+              file=sys.stderr, flush=True)
+    return dict(config="ahead-of-time tile configuration, n and k compiled in", cache=binding.fp8_jit_get_cache_dir(),
+                stats=binding.fp8_jit_stats(), by_shape=out)
 
 
 GROUPED = {

@@ -33,26 +33,16 @@ void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
                      dim3(64 * WMW * WNW * WK), 0, s, p);
 }
 
-// FMT: bit 0 = LHS in E5M2, bit 1 = RHS in E5M2.  The E4M3 x E4M3 build has
-// every shape; the other format pairs have the shapes dense_config picks by
-// itself (a forced shape falls back to those).
+// FMT: bit 0 = LHS in E5M2, bit 1 = RHS in E5M2.
 template <bool SPLIT, int FMT>
 void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
-  if constexpr (FMT == 0) {
-    switch (kind) {
-      case kS64N64: launch_gemm<64, 64, 1, 4, 4, kDense, SPLIT>(p, grid, s); return;
-      case kS64N128: launch_gemm<64, 128, 1, 4, 4, kDense, SPLIT>(p, grid, s); return;
-      case kS128N128: launch_gemm<128, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); return;
-      case kMid: launch_gemm<256, 128, 2, 2, 3, kDense, SPLIT>(p, grid, s); return;
-      default: break;
-    }
-  }
   switch (kind) {
     case kS128N64: launch_gemm<128, 64, 2, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kS64N32: launch_gemm<64, 32, 2, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kS128N32: launch_gemm<128, 32, 4, 1, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kS64N32K4: launch_gemm<64, 32, 1, 1, 3, kDense, SPLIT, 4, 4, FMT>(p, grid, s); break;
-    case kS128N32K2: launch_gemm<128, 32, 2, 1, 3, kDense, SPLIT, 2, 2, FMT>(p, grid, s); break;
+    case kF64N32: launch_gemm<64, 32, 4, 1, 4, kDense, SPLIT, 2, 1, FMT>(p, grid, s); break;
+    case kF64N64: launch_gemm<64, 64, 2, 2, 4, kDense, SPLIT, 2, 2, FMT>(p, grid, s); break;
+    case kF64N128: launch_gemm<64, 128, 4, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
+    case kF128N64: launch_gemm<128, 64, 4, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
+    case kF128N128: launch_gemm<128, 128, 4, 2, 3, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
     default:
       // the 256 x 256 tile cannot stage a split partial (dense_config never
       // asks for it)
@@ -156,9 +146,9 @@ int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales,
     return FP8G_EINVAL;
   if (int st = check_ld(lhs_scales_ld, m)) return st;
 
-  DenseConfig c = dense_config(m, n, k, true, fmt == 0);
+  DenseConfig c = dense_config(m, n, k, true);
   if (c.splits > 1 && (!workspace || workspace_bytes < dense_workspace(c, m, n)))
-    c = dense_config(m, n, k, false, fmt == 0);
+    c = dense_config(m, n, k, false);
 
   GemmParams p{};
   p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;

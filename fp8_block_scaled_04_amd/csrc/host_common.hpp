@@ -73,31 +73,24 @@ inline int check_ld(int64_t ld, int64_t rows) {
 // accumulator tile is at most 128 x 64 (128 VGPRs): the promotion FMAs need
 // their accumulators in architectural VGPRs.  The large-M shape runs two
 // waves per SIMD (eight per workgroup) so that one wave's LDS and barrier
-// waits are covered by the other's MFMAs.  Small-M shapes are HBM-bound:
-// narrow N tiles give enough workgroups; with few tiles per CU each wave
-// multiplies whole 64 x 32 tiles of its own K groups (ku = wk = 4), which
-// keeps more independent MFMAs in flight per stage; with many tiles per CU,
-// several small workgroups share a CU instead.  When the tile count would
-// leave CUs idle, K is split across workgroups; the last workgroup to finish
-// a tile adds the partial sums in split order.
+// waits are covered by the other's MFMAs.  m <= 128 is HBM-bound and picks
+// among five tile families by the estimate in dense_config.
 struct KernelShape {
   int bm, bn, stages, waves, ku;
   int wm, wn, wk;  // wave grid: waves along M and N, and waves sharing a sub-tile
 };
-enum DenseKind { kS64N64 = 0, kS64N128 = 1, kS128N64 = 2, kS128N128 = 3, kBig = 4, kMid = 5, kS64N32 = 6,
-                 kS128N32 = 7, kS64N32K4 = 8, kS128N32K2 = 9, kKinds = 10 };
+enum DenseKind { kBig = 0, kS128N64 = 1, kF64N32 = 2, kF64N64 = 3, kF64N128 = 4, kF128N64 = 5, kF128N128 = 6,
+                 kKinds = 7 };
 constexpr KernelShape kShapes[kKinds] = {
-    {64, 64, 4, 4, 1, 1, 4, 1},    // m <= 64
-    {64, 128, 4, 4, 1, 1, 4, 1},
-    {128, 64, 4, 4, 1, 2, 2, 1},   // 64 < m <= 128
-    {128, 128, 3, 4, 1, 2, 2, 1},
     {256, 256, 2, 8, 1, 4, 2, 1},  // m > 128
-    {256, 128, 3, 4, 1, 2, 2, 1},
-    {64, 32, 4, 4, 1, 2, 2, 1},
-    {128, 32, 4, 4, 1, 4, 1, 1},
-    {64, 32, 3, 4, 4, 1, 1, 4},    // m <= 64, few tiles per CU: four waves, four K groups per stage
-    {128, 32, 3, 4, 2, 2, 1, 2},   // 64 < m <= 128, few tiles per CU
+    {128, 64, 4, 4, 1, 2, 2, 1},   // m > 128 with few 256 x 256 tiles (split-K)
+    {64, 32, 4, 4, 2, 4, 1, 1},    // m <= 128 families
+    {64, 64, 4, 8, 2, 2, 2, 2},
+    {64, 128, 4, 8, 1, 4, 2, 1},
+    {128, 64, 4, 8, 1, 4, 2, 1},
+    {128, 128, 3, 8, 1, 4, 2, 1},
 };
+constexpr int kSmallFamilies[] = {kF64N32, kF64N64, kF64N128, kF128N64, kF128N128};
 // The grouped kernels' shapes: contiguous 256 x 256 tiles (one or two
 // 128-row blocks of one group), masked 128 x 128 tiles.
 constexpr KernelShape kContiguousShape = {256, 256, 2, 8, 1, 4, 2, 1};
@@ -113,33 +106,71 @@ inline int env_int(const char* name, int fallback) {
   return (v && *v) ? std::atoi(v) : fallback;
 }
 
-inline DenseConfig dense_config(int m, int n, int k, bool allow_split, bool all_kinds = true) {
+// Split count of a configuration: the K groups are dealt in equal runs, so
+// the count is rounded to what those runs give.
+inline int whole_splits(int kg, int s) { return int(cdiv(kg, cdiv(kg, std::max(1, std::min(s, kg))))); }
+
+// m <= 128: every workgroup streams its K range of BM LHS rows and BN RHS
+// rows through LDS, and the time goes with the busiest CU.  Candidates run
+// at most one workgroup per CU (measured: a second round of workgroups
+// costs more than any tile choice saves); among them the estimate
+//     K groups per workgroup * (BM / 2 + BN) * 128 B / 80 GB/s
+//     + 1 us per split when K is split (the split-K fix-up)
+// is least.  (The LHS rows are shared by all workgroups of a column and are
+// read from L2, hence half weight; the constants are per-CU copy rate and
+// fix-up latency measured on MI355X.)  If no family fits in one round, the
+// one with the fewest tiles runs unsplit.
+inline void small_m_choice(int m, int n, int kg, int cus, bool allow_split, int* kind, int* splits) {
+  double best = 0.0;
+  int best_kind = -1, best_splits = 1, fewest_kind = -1;
+  int64_t fewest = 0;
+  for (int f : kSmallFamilies) {
+    const KernelShape& ks = kShapes[f];
+    if (m <= 64 && ks.bm > 64) continue;
+    const int64_t tiles = cdiv(m, ks.bm) * cdiv(n, ks.bn);
+    if (fewest_kind < 0 || tiles < fewest) { fewest = tiles; fewest_kind = f; }
+    for (int s0 : {1, 2, 3, 4, 6, 8}) {
+      const int s = whole_splits(kg, s0);
+      if ((s > 1 && !allow_split) || (s0 > 1 && s == 1) || tiles * s > cus) continue;
+      const double t = double(cdiv(kg, s)) * (0.5 * ks.bm + ks.bn) * 128.0 / 80e9 +
+                       (s > 1 ? 1e-6 * s : 0.0);
+      if (best_kind < 0 || t < best) { best = t; best_kind = f; best_splits = s; }
+    }
+  }
+  *kind = best_kind >= 0 ? best_kind : fewest_kind;
+  *splits = best_kind >= 0 ? best_splits : 1;
+}
+
+inline DenseConfig dense_config(int m, int n, int k, bool allow_split) {
   DenseConfig c{};
-  const int cus0 = effective_cus();
-  // few 32-column tiles per CU: the K-group-sharing shapes; many: the plain ones
-  const bool few = cdiv(n, 32) < 2 * int64_t(cus0);
-  c.kind = m <= 64 ? (few ? kS64N32K4 : kS64N32) : (m <= 128 ? (few ? kS128N32K2 : kS128N32) : kBig);
-  // large M but few 256 x 256 tiles: narrower tiles with split-K fill the CUs
-  if (c.kind == kBig && cdiv(m, 256) * cdiv(n, 256) < cus0 / 2) c.kind = kS128N64;
+  const int cus = effective_cus();
+  const int kg = k / 128;
+  int splits = 1;
+  if (m <= 128) {
+    small_m_choice(m, n, kg, cus, allow_split, &c.kind, &splits);
+  } else {
+    c.kind = kBig;
+    // large M but few 256 x 256 tiles: narrower tiles with split-K fill the CUs
+    if (cdiv(m, 256) * cdiv(n, 256) < cus / 2) c.kind = kS128N64;
+  }
   const int forced = env_int("FP8G_FORCE_CONFIG", -1);  // debugging and tuning only
-  if (forced >= 0 && forced < kKinds && all_kinds) c.kind = forced;
+  if (forced >= 0 && forced < kKinds) c.kind = forced;
   const KernelShape& ks = kShapes[c.kind];
   c.tiles_m = int(cdiv(m, ks.bm));
   c.tiles_n = int(cdiv(n, ks.bn));
-  const int kg = k / 128;
-  c.splits = 1;
-  c.gps = kg;
   const int64_t tiles = int64_t(c.tiles_m) * c.tiles_n;
-  const int cus = effective_cus();
   const bool can_split = ks.bm * (ks.bn + 4) * 4 <= ks.stages * ks.ku * (ks.bm + ks.bn) * 128;  // staged tile fits the ring
-  // Split only when it at least doubles the workgroup count: each split
-  // adds a partial-sum round trip through memory at the end of the kernel.
-  if (allow_split && can_split && 2 * tiles <= cus + tiles / 2) {
-    int s = int(std::min<int64_t>(kg, (cus + tiles / 2) / tiles));
-    s = std::max(1, std::min(std::min(kg, kMaxSplits), env_int("FP8G_SPLITS", s)));
-    c.gps = int(cdiv(kg, s));
-    c.splits = int(cdiv(kg, c.gps));
+  if (m > 128 || forced >= 0) {
+    // Split only when it at least doubles the workgroup count: each split
+    // adds a partial-sum round trip through memory at the end of the kernel.
+    splits = 1;
+    if (allow_split && can_split && 2 * tiles <= cus + tiles / 2)
+      splits = int(std::min<int64_t>(kg, (cus + tiles / 2) / tiles));
   }
+  if (!allow_split || !can_split) splits = 1;
+  splits = std::max(1, std::min(std::min(kg, kMaxSplits), env_int("FP8G_SPLITS", splits)));
+  c.gps = int(cdiv(kg, splits));
+  c.splits = int(cdiv(kg, c.gps));
   return c;
 }
 

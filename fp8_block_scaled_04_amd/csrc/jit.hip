@@ -119,9 +119,9 @@ bool make_dirs(const std::string& path) {
   return true;
 }
 
-// Target of the current device ("gfx950:sramecc+:xnack-"), or gfx950 when
-// there is none (compile-only use: the disk cache can be filled without a
-// device).
+// Target of the current device ("gfx950:sramecc+:xnack-").  With no device
+// (compile-only use: filling a disk cache, e.g. for another machine) it is
+// $FP8G_JIT_TARGET, else gfx950.
 std::string device_arch(int* device) {
   int dev = -1;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -133,6 +133,7 @@ std::string device_arch(int* device) {
   }
   (void)hipGetLastError();
   *device = -1;
+  if (const char* t = std::getenv("FP8G_JIT_TARGET"); t && *t) return t;
   return "gfx950";
 }
 

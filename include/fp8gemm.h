@@ -164,7 +164,10 @@ int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
  * key, size or checksum is ignored, counted and replaced.  The first call
  * for a configuration therefore compiles (about a second) or reads the
  * disk; later calls only launch.  FP8G_JIT_DEBUG=1 reports compilations and
- * cache use on stderr.  Results equal the ahead-of-time kernels' for the
+ * cache use on stderr; FP8G_JIT_COMPILER names the compiler (default
+ * $ROCM_PATH/llvm/bin/clang++); without a device, FP8G_JIT_TARGET names the
+ * target to build for (default gfx950), so a cache can be filled ahead of
+ * time for another machine.  Results equal the ahead-of-time kernels' for the
  * same configuration. */
 enum { FP8G_JIT_DENSE = 0, FP8G_JIT_CONTIGUOUS = 1, FP8G_JIT_MASKED = 2 };
 

@@ -31,6 +31,30 @@ def test_dense_every_output(m, n, k):
         assert_close(got, ref, f"m={m} n={n} k={k} ws={ws}")
 
 
+# (shape, tile the library picks, split): every m <= 128 tile family, split
+# and unsplit, with M and N tails
+FAMILY_CASES = [((1, 8, 7168), "64x32", True), ((37, 2112, 1024), "64x32", False),
+                ((1, 8200, 128), "64x64", False), ((16, 7168, 12288), "64x64", True),
+                ((1, 16392, 128), "64x128", False), ((1, 8200, 7168), "64x128", True),
+                ((65, 8200, 128), "128x64", False), ((65, 7168, 7168), "128x64", True),
+                ((65, 16392, 128), "128x128", False), ((65, 8200, 4096), "128x128", True)]
+
+
+@pytest.mark.parametrize("shape,tile,split", FAMILY_CASES)
+def test_dense_small_m_tile_families_every_output(shape, tile, split):
+    require_gpu()
+    m, n, k = shape
+    desc = binding.fp8_gemm_describe(m, n, k)
+    assert desc.startswith(f"tile={tile} ") and ("splits=1 " not in desc) == split, desc
+    say(f"dense family {desc} m={m} n={n} k={k}")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=n + k)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    got = run_dense(qa, sa, qb, sb)
+    assert_close(got, ref, f"{m}x{n}x{k} {desc}")
+    if split:
+        assert np.array_equal(got, run_dense(qa, sa, qb, sb)), "split-K result not deterministic"
+
+
 def test_dense_k_tail_regression_shape():
     """The K-tail failure shape of the jianying88 practice article (§6.1):
     M = N = 6144, K = 1280, checked on sampled outputs."""
@@ -87,7 +111,8 @@ def test_dense_config4_outliers_sampled(m, n, k):
 
 def test_dense_split_and_unsplit_agree_and_are_deterministic():
     require_gpu()
-    qa, sa, qb, sb = dense_case(64, 1024, 4096, seed=5)
+    assert "splits=3 " in binding.fp8_gemm_describe(8, 1024, 8192)
+    qa, sa, qb, sb = dense_case(8, 1024, 8192, seed=5)
     a = run_dense(qa, sa, qb, sb, use_workspace=True)
     b = run_dense(qa, sa, qb, sb, use_workspace=True)
     c = run_dense(qa, sa, qb, sb, use_workspace=False)
@@ -156,7 +181,7 @@ def _dense_dev(qa, sa, qb, sb):
     return dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb)
 
 
-@pytest.mark.parametrize("m,n,k", [(64, 1024, 4096), (128, 512, 7168)])
+@pytest.mark.parametrize("m,n,k", [(8, 1024, 8192), (128, 512, 7168)])
 def test_splitk_workspace_needs_no_initialisation(m, n, k):
     """The split-K arrival counters are tagged per call: a workspace full of
     random bytes gives the same bits as a zeroed one, call after call."""
@@ -183,6 +208,7 @@ def test_splitk_graph_replay_matches_eager():
     between, reproduces the eager result bit for bit each time."""
     require_gpu()
     m, n, k = 64, 2048, 7168
+    assert "splits=1 " not in binding.fp8_gemm_describe(m, n, k)
     qa, sa, qb, sb = dense_case(m, n, k, seed=12)
     a, s_, b, t = _dense_dev(qa, sa, qb, sb)
     ws = torch.zeros(binding.fp8_gemm_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device="cuda")

@@ -224,15 +224,16 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
   p.masked_m = masked_m;
   p.sa_ld = lhs_scales_ld;
   p.m = max_m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
-  // 128-row tiles: a group's second row tile exits at once when its count
-  // is at most 128 (the usual decode case), so most RHS tiles are read once.
-  p.tiles_m = int(cdiv(max_m, 128)); p.tiles_n = int(cdiv(n, 128)); p.splits = 1; p.groups_per_split = p.kg;
+  // Row tiles past a group's count exit at once; the RHS tile of a group is
+  // read by each of its live row tiles (mostly from L2).
+  p.tiles_m = int(cdiv(max_m, kMaskedShape.bm)); p.tiles_n = int(cdiv(n, kMaskedShape.bn)); p.splits = 1;
+  p.groups_per_split = p.kg;
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n * num_groups;
   if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] masked G=%d max_m=%d n=%d k=%d grid=%lld\n", num_groups, max_m, n, k,
                  (long long)grid);
-  launch_gemm<128, 128, 2, 2, 4, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
+  launch_gemm<64, 128, 1, 4, 3, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
   return launched("masked gemm");
 }
 

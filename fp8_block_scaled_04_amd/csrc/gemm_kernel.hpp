@@ -294,7 +294,14 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   constexpr int SB_BLOCKS = (BN + 127) / 128;  // RHS scale blocks a tile touches
   static_assert(RING + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[RING];
+  // After the K loop the ring holds the BF16 output tile on its way out
+  // (rows padded by 8 elements so that neither the fragment-ordered writes
+  // nor the row-ordered reads pile onto a few banks).
+  constexpr int OUT_LDT = BN + 8;
+  constexpr int OUT_BYTES = BM * OUT_LDT * 2;
+  constexpr int SMEM = RING > OUT_BYTES ? RING : OUT_BYTES;
+  static_assert(SMEM + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS with the output staging");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ float sb_cache[SB_BLOCKS][kMaxGroups];
 
   static_assert(NSPEC >= 0 && NSPEC % 8 == 0 && KSPEC >= 0 && KSPEC % kGroupK == 0 &&
@@ -581,20 +588,32 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
       }
     }
   } else {
-    if (!holder) return;
+    // The tile goes out through LDS: a lane's accumulators are 4 columns of
+    // one row per sub-tile, so stored directly each instruction would write
+    // 32 bytes into each of 16 rows; staged, every instruction writes whole
+    // rows in 16-byte pieces (measured: the output burst at the end of a
+    // round of large-M tiles drains about twice as fast).
+    uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
+    __syncthreads();  // every wave is done with the ring (and with the partial-tile sums)
+    if (holder) {
 #pragma unroll
-    for (int i = 0; i < TN; ++i) {
-      const int col = n0 + wrow_n + 16 * i + 4 * (lane >> 4);
+      for (int i = 0; i < TN; ++i)
 #pragma unroll
-      for (int j = 0; j < TM; ++j) {
-        const int tok = m0 + wrow_m + 16 * j + (lane & 15);
-        if (tok < rows && col < shape_n) {
+        for (int j = 0; j < TM; ++j) {
           uint2 v;
           v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
           v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-          *reinterpret_cast<uint2*>(OUT + int64_t(tok) * shape_n + col) = v;
+          *reinterpret_cast<uint2*>(stage + (wrow_m + 16 * j + (lane & 15)) * OUT_LDT + wrow_n + 16 * i +
+                                    4 * (lane >> 4)) = v;
         }
-      }
+    }
+    __syncthreads();
+    constexpr int CHUNKS = BN / 8;  // 16-byte pieces per tile row (n % 8 == 0: a piece is all in or all out)
+    for (int c = threadIdx.x; c < BM * CHUNKS; c += blockDim.x) {
+      const int r = c / CHUNKS, col = n0 + 8 * (c % CHUNKS);
+      if (m0 + r < rows && col < shape_n)
+        *reinterpret_cast<uint4*>(OUT + int64_t(m0 + r) * shape_n + col) =
+            *reinterpret_cast<const uint4*>(stage + r * OUT_LDT + 8 * (c % CHUNKS));
     }
   }
 }

@@ -165,7 +165,8 @@ bool valid_config(const fp8_gemm_config& c, int mode) {
   const int slots = c.stages * c.k_per_stage;
   const int ring = slots * (c.block_m * 128 + c.block_n * 128 + c.block_m * 4);
   const int sb_blocks = (c.block_n + 127) / 128;
-  if (ring + sb_blocks * fp8g::kMaxGroups * 4 > 160 * 1024) return false;  // LDS
+  const int staging = c.block_m * (c.block_n + 8) * 2;  // the BF16 output tile on its way out
+  if (std::max(ring, staging) + sb_blocks * fp8g::kMaxGroups * 4 > 160 * 1024) return false;  // LDS
   const int tm = wm / 16, tn = wn / 16;
   if (tm * tn > 32) return false;  // accumulators stay within 128 VGPRs
   if (c.waves_k > 1 && nw * tn * tm * 64 * 16 > ring) return false;

@@ -32,12 +32,14 @@
 
 #include <atomic>
 #include <chrono>
+#include <condition_variable>
 #include <cerrno>
 #include <cstring>
 #include <fstream>
 #include <mutex>
 #include <string>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include "fp8gemm.h"
@@ -86,8 +88,10 @@ uint64_t source_digest() {
   return d;
 }
 
-std::mutex g_mu;
-std::string g_cache_dir;  // empty: not chosen yet
+std::mutex g_mu;                          // guards the tables below
+std::condition_variable g_built;          // a kernel left g_building
+std::unordered_set<std::string> g_building;  // kernels being read, compiled or loaded
+std::string g_cache_dir;                  // empty: not chosen yet
 
 std::string compiler_path() {
   if (const char* c = std::getenv("FP8G_JIT_COMPILER"); c && *c) return c;
@@ -422,46 +426,62 @@ int compile(const std::string& dir, const std::string& arch, const std::string& 
 
 // The kernel for `prog` on the current device: from memory, else from the
 // disk cache, else compiled (and written to the cache).  With no device the
-// code object is only made available on disk and *fn stays null.
+// code object is only made available on disk and *fn stays null.  The lock
+// covers only the tables: a compilation runs unlocked, so other kernels stay
+// usable meanwhile, and a second caller of the same kernel waits for the
+// first instead of compiling it again.
 int get_kernel(const Program& prog, hipFunction_t* fn) {
   *fn = nullptr;
-  std::lock_guard<std::mutex> lock(g_mu);
   int device = -1;
   const std::string arch = device_arch(&device);
   const std::string key = cache_key(arch, prog);
   const std::string mem_key = std::to_string(device) + "|" + key;
-  if (device >= 0) {
-    auto it = g_loaded.find(mem_key);
-    if (it != g_loaded.end()) {
-      g_stat[kMemHit]++;
-      *fn = it->second.fn;
-      return FP8G_OK;
+  std::string dir;
+  {
+    std::unique_lock<std::mutex> lock(g_mu);
+    g_built.wait(lock, [&] { return g_building.count(mem_key) == 0; });
+    if (device >= 0) {
+      auto it = g_loaded.find(mem_key);
+      if (it != g_loaded.end()) {
+        g_stat[kMemHit]++;
+        *fn = it->second.fn;
+        return FP8G_OK;
+      }
     }
+    g_building.insert(mem_key);
+    dir = cache_dir_locked();
   }
-  const std::string& dir = cache_dir_locked();
-  const std::string path = cache_file(dir, key);
-  std::string name;
-  std::vector<char> code;
-  bool rejected = false;
-  if (read_cached(path, key, &name, &code, &rejected) && name == prog.symbol) {
-    g_stat[kDiskHit]++;
-    if (jit_debug()) std::fprintf(stderr, "[fp8gemm jit] %s from %s\n", prog.expr.c_str(), path.c_str());
-  } else {
-    if (rejected) g_stat[kRejected]++;
-    if (const int st = compile(dir, arch, key, prog, &code)) return st;
-    name = prog.symbol;
-    write_cached(dir, path, key, name, code);
-  }
-  if (device < 0) return FP8G_OK;
   Loaded l;
-  if (hipModuleLoadData(&l.module, code.data()) != hipSuccess ||
-      hipModuleGetFunction(&l.fn, l.module, name.c_str()) != hipSuccess) {
-    (void)hipGetLastError();
-    return FP8G_ELAUNCH;
+  const int st = [&] {
+    const std::string path = cache_file(dir, key);
+    std::string name;
+    std::vector<char> code;
+    bool rejected = false;
+    if (read_cached(path, key, &name, &code, &rejected) && name == prog.symbol) {
+      g_stat[kDiskHit]++;
+      if (jit_debug()) std::fprintf(stderr, "[fp8gemm jit] %s from %s\n", prog.expr.c_str(), path.c_str());
+    } else {
+      if (rejected) g_stat[kRejected]++;
+      if (const int c = compile(dir, arch, key, prog, &code)) return c;
+      name = prog.symbol;
+      write_cached(dir, path, key, name, code);
+    }
+    if (device < 0) return int(FP8G_OK);
+    if (hipModuleLoadData(&l.module, code.data()) != hipSuccess ||
+        hipModuleGetFunction(&l.fn, l.module, name.c_str()) != hipSuccess) {
+      (void)hipGetLastError();
+      return int(FP8G_ELAUNCH);
+    }
+    return int(FP8G_OK);
+  }();
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (st == FP8G_OK && l.fn) g_loaded[mem_key] = l;  // kept until the process ends
+    g_building.erase(mem_key);
   }
-  g_loaded[mem_key] = l;  // kept until the process ends
+  g_built.notify_all();
   *fn = l.fn;
-  return FP8G_OK;
+  return st;
 }
 
 int launch(const Program& prog, const GemmParams& p, int64_t grid, void* stream) {

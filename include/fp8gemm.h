@@ -167,7 +167,10 @@ int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
  * cache use on stderr; FP8G_JIT_COMPILER names the compiler (default
  * $ROCM_PATH/llvm/bin/clang++); without a device, FP8G_JIT_TARGET names the
  * target to build for (default gfx950), so a cache can be filled ahead of
- * time for another machine.  Results equal the ahead-of-time kernels' for the
+ * time for another machine.  Calls are thread-safe; a first call of a
+ * configuration compiles or loads a module, which is not a stream operation:
+ * warm a configuration up (fp8_jit_warmup or one call) before capturing its
+ * calls in a HIP graph.  Results equal the ahead-of-time kernels' for the
  * same configuration. */
 enum { FP8G_JIT_DENSE = 0, FP8G_JIT_CONTIGUOUS = 1, FP8G_JIT_MASKED = 2 };
 

@@ -188,3 +188,29 @@ def test_cache_dir_default_and_override(lib, monkeypatch, tmp_path):
         assert binding.fp8_jit_get_cache_dir() == str(tmp_path / ".cache" / "fp8gemm")
     finally:
         binding.fp8_jit_set_cache_dir(prev)
+
+
+def test_concurrent_warmups_compile_each_kernel_once(cache):
+    """Threads asking for the same kernels at once: one compilation per kernel
+    (the others wait for it and read the result), different kernels compile
+    side by side."""
+    import threading
+    configs = [cfg(block_n=64, stages=2), cfg(block_n=64, stages=3)]
+    errors = []
+
+    def work(c):
+        try:
+            binding.fp8_jit_warmup(D, 1024, 1024, config=c)
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append(e)
+
+    before = binding.fp8_jit_stats()
+    threads = [threading.Thread(target=work, args=(configs[i % 2],)) for i in range(6)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    d = delta(before, binding.fp8_jit_stats())
+    assert not errors
+    assert d["compiles"] == 2 and d["disk_hits"] == 4 and d["failed_compiles"] == 0
+    assert len(code_files(cache)) == 2

@@ -142,3 +142,38 @@ def test_unsupported_config_fails_before_launch():
     with pytest.raises(binding.Fp8GemmError) as e:
         run_jit(qa, sa, qb, sb, config=bad, workspace=False)
     assert e.value.status == binding.FP8G_EUNSUPPORTED
+
+
+def test_warmed_up_jit_call_replays_in_a_graph():
+    """A warmed-up runtime-specialised split-K call captured in a HIP graph and
+    replayed several times, with eager work between replays, gives the eager
+    bits every time."""
+    require_gpu()
+    m, n, k = 64, 2048, 4096
+    qa, sa, qb, sb = dense_case(m, n, k, seed=13)
+    config = dict(CONFIGS[0], specialize=1)
+    binding.fp8_jit_warmup(D, n, k, config=config)
+    a, s_, b, t = dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb)
+    ws = torch.empty(binding.fp8_jit_gemm_workspace_bytes(m, n, k, config) // 4 + 1, dtype=torch.float32,
+                     device="cuda")
+    eager = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    binding.fp8_jit_gemm_nt(a, E4, s_, b, E4, t, eager, config=config, workspace=ws)
+    torch.cuda.synchronize()
+    ref = eager.view(torch.int16).cpu().numpy()
+    out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        binding.fp8_jit_gemm_nt(a, E4, s_, b, E4, t, out, config=config, workspace=ws)  # on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        binding.fp8_jit_gemm_nt(a, E4, s_, b, E4, t, out, config=config, workspace=ws)
+    for r in range(4):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref), f"replay {r}"
+        binding.fp8_jit_gemm_nt(a, E4, s_, b, E4, t, eager, config=config, workspace=ws)   # eager work between
+        torch.cuda.synchronize()

@@ -41,7 +41,6 @@ void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
     case kF64N32: launch_gemm<64, 32, 4, 1, 4, kDense, SPLIT, 2, 1, FMT>(p, grid, s); break;
     case kF64N64: launch_gemm<64, 64, 2, 2, 4, kDense, SPLIT, 2, 2, FMT>(p, grid, s); break;
     case kF64N128: launch_gemm<64, 128, 4, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kF128N64: launch_gemm<128, 64, 4, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
     case kF128N128: launch_gemm<128, 128, 4, 2, 3, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
     default:
       // the 256 x 256 tile cannot stage a split partial (dense_config never

@@ -74,23 +74,21 @@ inline int check_ld(int64_t ld, int64_t rows) {
 // their accumulators in architectural VGPRs.  The large-M shape runs two
 // waves per SIMD (eight per workgroup) so that one wave's LDS and barrier
 // waits are covered by the other's MFMAs.  m <= 128 is HBM-bound and picks
-// among five tile families by the estimate in dense_config.
+// among four tile families by the estimate in dense_config.
 struct KernelShape {
   int bm, bn, stages, waves, ku;
   int wm, wn, wk;  // wave grid: waves along M and N, and waves sharing a sub-tile
 };
-enum DenseKind { kBig = 0, kS128N64 = 1, kF64N32 = 2, kF64N64 = 3, kF64N128 = 4, kF128N64 = 5, kF128N128 = 6,
-                 kKinds = 7 };
+enum DenseKind { kBig = 0, kS128N64 = 1, kF64N32 = 2, kF64N64 = 3, kF64N128 = 4, kF128N128 = 5, kKinds = 6 };
 constexpr KernelShape kShapes[kKinds] = {
     {256, 256, 2, 8, 1, 4, 2, 1},  // m > 128
     {128, 64, 4, 4, 1, 2, 2, 1},   // m > 128 with few 256 x 256 tiles (split-K)
     {64, 32, 4, 4, 2, 4, 1, 1},    // m <= 128 families
     {64, 64, 4, 8, 2, 2, 2, 2},
     {64, 128, 4, 8, 1, 4, 2, 1},
-    {128, 64, 4, 8, 1, 4, 2, 1},
     {128, 128, 3, 8, 1, 4, 2, 1},
 };
-constexpr int kSmallFamilies[] = {kF64N32, kF64N64, kF64N128, kF128N64, kF128N128};
+constexpr int kSmallFamilies[] = {kF64N32, kF64N64, kF64N128, kF128N128};
 // The grouped kernels' shapes: contiguous 256 x 256 tiles (one or two
 // 128-row blocks of one group); masked 64 x 128 tiles, so that slots that
 // are mostly empty (decode) waste few rows (measured: 12% faster than
@@ -116,12 +114,13 @@ inline int whole_splits(int kg, int s) { return int(cdiv(kg, cdiv(kg, std::max(1
 // rows through LDS, and the time goes with the busiest CU.  Candidates run
 // at most one workgroup per CU (measured: a second round of workgroups
 // costs more than any tile choice saves); among them the estimate
-//     K groups per workgroup * (BM / 2 + BN) * 128 B / 80 GB/s
-//     + 1 us per split when K is split (the split-K fix-up)
-// is least.  (The LHS rows are shared by all workgroups of a column and are
-// read from L2, hence half weight; the constants are per-CU copy rate and
-// fix-up latency measured on MI355X.)  If no family fits in one round, the
-// one with the fewest tiles runs unsplit.
+//     K groups per workgroup * (BM + BN) * 128 B / 80 GB/s
+//     + (when K is split into s) s * 1 us + s * m * n * 8 B / 4 TB/s
+// is least: the per-CU copy rate, the fix-up latency and the partial sums'
+// round trip through memory, as measured on MI355X.  Over 24 shapes (m in
+// 32..128, n 1536..32768, k 512..16384) the pick was within 7% of the best
+// of 218 tile configurations x split counts, 1.4% on average.  If no family
+// fits in one round, the one with the fewest tiles runs unsplit.
 inline void small_m_choice(int m, int n, int kg, int cus, bool allow_split, int* kind, int* splits) {
   double best = 0.0;
   int best_kind = -1, best_splits = 1, fewest_kind = -1;
@@ -134,8 +133,8 @@ inline void small_m_choice(int m, int n, int kg, int cus, bool allow_split, int*
     for (int s0 : {1, 2, 3, 4, 6, 8}) {
       const int s = whole_splits(kg, s0);
       if ((s > 1 && !allow_split) || (s0 > 1 && s == 1) || tiles * s > cus) continue;
-      const double t = double(cdiv(kg, s)) * (0.5 * ks.bm + ks.bn) * 128.0 / 80e9 +
-                       (s > 1 ? 1e-6 * s : 0.0);
+      const double t = double(cdiv(kg, s)) * double(ks.bm + ks.bn) * 128.0 / 80e9 +
+                       (s > 1 ? 1e-6 * s + double(s) * m * n * 8.0 / 4e12 : 0.0);
       if (best_kind < 0 || t < best) { best = t; best_kind = f; best_splits = s; }
     }
   }

@@ -120,9 +120,9 @@ def run(qa, sa, qb, sb, a_fmt, b_fmt, use_workspace=True):
     return out.result()
 
 
-# one shape per tile family the library picks by itself: 64 x 32 (split and
-# not), 64 x 64, 64 x 128, 128 x 64, 128 x 128, then 128 x 64 with split-K
-# (m > 128, few tiles) and 256 x 256
+# one shape per tile family the library picks by itself: 64 x 32 (unsplit
+# and split), 64 x 64, 64 x 128 (one and two row tiles), 128 x 128, then
+# 128 x 64 with split-K (m > 128, few tiles) and 256 x 256
 SHAPES = [(37, 2112, 1024), (1, 8, 7168), (1, 8200, 128), (64, 16392, 512), (65, 8200, 128), (128, 16392, 256),
           (300, 520, 1024), (2560, 3328, 128)]
 

@@ -34,10 +34,11 @@ def test_dense_every_output(m, n, k):
 # (shape, tile the library picks, split): every m <= 128 tile family, split
 # and unsplit, with M and N tails
 FAMILY_CASES = [((1, 8, 7168), "64x32", True), ((37, 2112, 1024), "64x32", False),
-                ((1, 8200, 128), "64x64", False), ((16, 7168, 12288), "64x64", True),
+                ((1, 8200, 128), "64x64", False), ((1, 4096, 12288), "64x64", True),
+                ((16, 7168, 12288), "64x64", True), ((65, 7168, 7168), "64x64", False),
                 ((1, 16392, 128), "64x128", False), ((1, 8200, 7168), "64x128", True),
-                ((65, 8200, 128), "128x64", False), ((65, 7168, 7168), "128x64", True),
-                ((65, 16392, 128), "128x128", False), ((65, 8200, 4096), "128x128", True)]
+                ((65, 8200, 128), "64x128", False), ((65, 16392, 128), "128x128", False),
+                ((65, 8200, 7168), "128x128", True)]
 
 
 @pytest.mark.parametrize("shape,tile,split", FAMILY_CASES)

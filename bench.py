@@ -92,8 +92,8 @@ def main():
         print(kernel_source_digest())
         return
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the path shards by N or by expert with no exchange inside the GEMM; see the design notes)",
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              f"(across GPUs the GEMM shards by N, by M or by expert, with no exchange inside it)",
               file=sys.stderr)
         sys.exit(2)
 

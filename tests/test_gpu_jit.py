@@ -53,7 +53,7 @@ def test_default_config_reproduces_the_ahead_of_time_bits(m, n, k):
     assert_close(aot, oracle.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
 
 
-CONFIGS = [
+TILE_CONFIGS = [
     dict(block_m=64, block_n=64, waves_m=1, waves_n=4, waves_k=1, stages=4, k_per_stage=1, splits=3),
     dict(block_m=128, block_n=128, waves_m=2, waves_n=2, waves_k=1, stages=3, k_per_stage=1, splits=1),
     dict(block_m=256, block_n=128, waves_m=2, waves_n=2, waves_k=1, stages=2, k_per_stage=1, splits=1),
@@ -64,10 +64,10 @@ CONFIGS = [
 
 
 @pytest.mark.parametrize("specialize", [0, 1])
-@pytest.mark.parametrize("ci", range(len(CONFIGS)))
+@pytest.mark.parametrize("ci", range(len(TILE_CONFIGS)))
 def test_tile_configs_match_the_oracle(ci, specialize):
     require_gpu()
-    config = dict(CONFIGS[ci], specialize=specialize)
+    config = dict(TILE_CONFIGS[ci], specialize=specialize)
     assert binding.fp8_jit_config_supported(D, config), config
     m, n, k = 200, 1032, 1664        # tails in M and N, 13 K groups (uneven splits)
     say(f"jit config {ci} specialize={specialize}")
@@ -126,7 +126,7 @@ def test_second_call_finds_the_kernel_loaded():
     require_gpu()
     m, n, k = 64, 512, 1024
     qa, sa, qb, sb = dense_case(m, n, k, seed=9)
-    config = dict(CONFIGS[1], specialize=1)
+    config = dict(TILE_CONFIGS[1], specialize=1)
     first = run_jit(qa, sa, qb, sb, config=config)
     before = binding.fp8_jit_stats()
     second = run_jit(qa, sa, qb, sb, config=config)
@@ -138,7 +138,7 @@ def test_second_call_finds_the_kernel_loaded():
 def test_unsupported_config_fails_before_launch():
     require_gpu()
     qa, sa, qb, sb = dense_case(16, 64, 256, seed=1)
-    bad = dict(CONFIGS[0], stages=9)
+    bad = dict(TILE_CONFIGS[0], stages=9)
     with pytest.raises(binding.Fp8GemmError) as e:
         run_jit(qa, sa, qb, sb, config=bad, workspace=False)
     assert e.value.status == binding.FP8G_EUNSUPPORTED
@@ -151,7 +151,7 @@ def test_warmed_up_jit_call_replays_in_a_graph():
     require_gpu()
     m, n, k = 64, 2048, 4096
     qa, sa, qb, sb = dense_case(m, n, k, seed=13)
-    config = dict(CONFIGS[0], specialize=1)
+    config = dict(TILE_CONFIGS[0], specialize=1)
     binding.fp8_jit_warmup(D, n, k, config=config)
     a, s_, b, t = dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb)
     ws = torch.empty(binding.fp8_jit_gemm_workspace_bytes(m, n, k, config) // 4 + 1, dtype=torch.float32,

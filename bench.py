@@ -585,7 +585,7 @@ def grouped_measurements(stream):
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "fp8_block_scaled_04_amd", "csrc", f)
-                  for f in ("gemm_kernel.hpp", "device_common.hpp", "fp8gemm.hip")]
+                  for f in ("gemm_kernel.hpp", "device_common.hpp", "host_common.hpp", "dense_launch.hip", "fp8gemm.hip")]
 
 
 def kernel_source_digest():

@@ -15,6 +15,7 @@
 #include "cast_kernel.hpp"
 #include "gemm_kernel.hpp"
 #include "host_common.hpp"
+#include "dense_launch.hpp"
 
 namespace {
 
@@ -33,30 +34,14 @@ void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
                      dim3(64 * WMW * WNW * WK), 0, s, p);
 }
 
-// FMT: bit 0 = LHS in E5M2, bit 1 = RHS in E5M2.
-template <bool SPLIT, int FMT>
-void launch_dense(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
-  switch (kind) {
-    case kS128N64: launch_gemm<128, 64, 2, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kF64N32: launch_gemm<64, 32, 4, 1, 4, kDense, SPLIT, 2, 1, FMT>(p, grid, s); break;
-    case kF64N64: launch_gemm<64, 64, 2, 2, 4, kDense, SPLIT, 2, 2, FMT>(p, grid, s); break;
-    case kF64N128: launch_gemm<64, 128, 4, 2, 4, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kF128N128: launch_gemm<128, 128, 4, 2, 3, kDense, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    default:
-      // the 256 x 256 tile cannot stage a split partial (dense_config never
-      // asks for it)
-      if constexpr (!SPLIT) launch_gemm<256, 256, 4, 2, 2, kDense, false, 1, 1, FMT>(p, grid, s);
-      break;
-  }
-}
-
-template <bool SPLIT>
-void launch_dense_fmt(int fmt, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+// The dense GEMM kernels are instantiated in dense_launch.hip, one object per
+// operand-format pair (FMT: bit 0 = LHS in E5M2, bit 1 = RHS in E5M2).
+void launch_dense_fmt(bool split, int fmt, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
   switch (fmt) {
-    case 1: launch_dense<SPLIT, 1>(kind, p, grid, s); break;
-    case 2: launch_dense<SPLIT, 2>(kind, p, grid, s); break;
-    case 3: launch_dense<SPLIT, 3>(kind, p, grid, s); break;
-    default: launch_dense<SPLIT, 0>(kind, p, grid, s); break;
+    case 1: fp8g::host::launch_dense_kind<1>(split, kind, p, grid, s); break;
+    case 2: fp8g::host::launch_dense_kind<2>(split, kind, p, grid, s); break;
+    case 3: fp8g::host::launch_dense_kind<3>(split, kind, p, grid, s); break;
+    default: fp8g::host::launch_dense_kind<0>(split, kind, p, grid, s); break;
   }
 }
 
@@ -164,11 +149,7 @@ int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales,
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
                  c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
-  if (c.splits > 1) {
-    launch_dense_fmt<true>(fmt, c.kind, p, grid, s);
-    return launched("gemm");
-  }
-  launch_dense_fmt<false>(fmt, c.kind, p, grid, s);
+  launch_dense_fmt(c.splits > 1, fmt, c.kind, p, grid, s);
   return launched("gemm");
 }
 

@@ -389,21 +389,29 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   // ---- HBM -> LDS copies: per-lane byte offsets are loop invariant --------
   // Copy i of this wave fills 1 KB unit u = i * NW + wave of the tile, i.e.
   // half u & 1 of 16-row block u >> 1: lane l fetches the row and logical
-  // chunk that tile_byte() places at byte 16 * l of that unit.
+  // chunk that tile_byte() places at byte 16 * l of that unit.  The 64-bit
+  // bases point at the tile's first row (and scale), so the 32-bit per-lane
+  // offsets stay below BM (or BN) rows of k bytes however large the operands
+  // are (an operand past 4 GiB would overflow offsets taken from its start).
+  const uint8_t* A_tile = A + int64_t(m0) * shape_k;
+  const uint8_t* B_tile = B + int64_t(n0) * shape_k;
+  const float* SA_tile = SA + m0;
   uint32_t a_off[A_COPIES], b_off[B_COPIES];
 #pragma unroll
   for (int i = 0; i < A_COPIES; ++i) {
     const int u = i * NW + wave;
     const int r = 16 * (u >> 1) + tile_row(u & 1, lane);
-    a_off[i] = uint32_t(min(m0 + r, rows - 1)) * uint32_t(shape_k) + 16u * tile_chunk(u & 1, lane);
+    a_off[i] = uint32_t(min(m0 + r, rows - 1) - m0) * uint32_t(shape_k) + 16u * tile_chunk(u & 1, lane);
   }
 #pragma unroll
   for (int i = 0; i < B_COPIES; ++i) {
     const int u = i * NW + wave;
     const int r = 16 * (u >> 1) + tile_row(u & 1, lane);
-    b_off[i] = uint32_t(min(n0 + r, shape_n - 1)) * uint32_t(shape_k) + 16u * tile_chunk(u & 1, lane);
+    b_off[i] = uint32_t(min(n0 + r, shape_n - 1) - n0) * uint32_t(shape_k) + 16u * tile_chunk(u & 1, lane);
   }
-  const uint32_t s_off = 4u * uint32_t(min(m0 + 4 * lane, int(p.sa_ld) - 4));
+  // (sa_ld >= rows and a multiple of 4, and m0 a multiple of 4 below rows:
+  // the clamped index is never below m0)
+  const uint32_t s_off = 4u * uint32_t(min(m0 + 4 * lane, int(p.sa_ld) - 4) - m0);
   const uint32_t lds0 = uniform(int(lds_addr(smem)));
   // Stage `it` holds groups g_begin + KU * it + u, u < KU; in a last,
   // partial stage the missing groups repeat the last one (never multiplied),
@@ -413,8 +421,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     static_for<0, KU>([&](auto uc) __attribute__((always_inline)) {
       constexpr int slot = stage * KU + decltype(uc)::value;
       const int g = uniform(min(g_begin + KU * it + decltype(uc)::value, g_end - 1));
-      const uint8_t* a_src = A + int64_t(g) * kGroupK;
-      const uint8_t* b_src = B + int64_t(g) * kGroupK;
+      const uint8_t* a_src = A_tile + int64_t(g) * kGroupK;
+      const uint8_t* b_src = B_tile + int64_t(g) * kGroupK;
 #pragma unroll
       for (int i = 0; i < A_COPIES; ++i)
         copy16_to_lds(a_src, a_off[i], lds0 + A_REGION + slot * A_BYTES + (i * NW + wave) * 1024);
@@ -422,7 +430,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
       for (int i = 0; i < B_COPIES; ++i)
         copy16_to_lds(b_src, b_off[i], lds0 + B_REGION + slot * B_BYTES + (i * NW + wave) * 1024);
       if (wave == 0 && lane < BM / 4)
-        copy16_to_lds(SA + int64_t(g) * p.sa_ld, s_off, lds0 + S_REGION + slot * S_BYTES);
+        copy16_to_lds(SA_tile + int64_t(g) * p.sa_ld, s_off, lds0 + S_REGION + slot * S_BYTES);
     });
   };
 

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 from fp8_block_scaled_04_amd import binding
-from _gpu import (assert_close, dense_case, dev, require_gpu, run_dense, sa_mn_major, sample_points,
+from _gpu import (assert_close, dense_case, dev, ld_of, require_gpu, run_dense, sa_mn_major, sample_points,
                   say, Guarded)
 
 pytestmark = pytest.mark.gpu
@@ -235,3 +235,83 @@ def test_splitk_graph_replay_matches_eager():
         # eager work between replays (also moves the counters' epoch on)
         binding.fp8_gemm_nt(a, s_, b, t, eager, workspace=ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m,n,k", [(16, 264, 65536), (200, 136, 65536)])
+def test_dense_maximum_k(m, n, k):
+    """k = 65536, the largest the kernels take (512 K groups, every RHS scale
+    row of a tile held in LDS): split and unsplit paths against the oracle."""
+    require_gpu()
+    say(f"dense maximum k m={m} n={n} k={k} {binding.fp8_gemm_describe(m, n, k)}")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=7)
+    ref = oracle.gemm_nt(qa, sa, qb, sb)
+    for ws in (True, False):
+        assert_close(run_dense(qa, sa, qb, sb, use_workspace=ws), ref, f"{m}x{n}x{k} ws={ws}")
+
+
+def test_dense_maximum_k_256_tile():
+    """The 256 x 256 tile (through the runtime specialisation, one tile) at k = 65536."""
+    require_gpu()
+    m, n, k = 256, 256, 65536
+    qa, sa, qb, sb = dense_case(m, n, k, seed=8)
+    config = dict(block_m=256, block_n=256, waves_m=4, waves_n=2, waves_k=1, stages=2, k_per_stage=1, splits=1,
+                  specialize=0)
+    out = Guarded((m, n))
+    binding.fp8_jit_gemm_nt(dev(qa), binding.FP8G_E4M3, dev(sa_mn_major(sa)), dev(qb), binding.FP8G_E4M3, dev(sb),
+                            out.view, config=config)
+    assert_close(out.result(), oracle.gemm_nt(qa, sa, qb, sb), "256x256x65536")
+
+
+def _device_codes(rows, k, seed):
+    """Seeded random E4M3 codes made on the device (an operand this large is
+    slow to make on the host): uniform over every finite code, NaN (0x7f,
+    0xff) excluded."""
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    c = torch.randint(0, 254, (rows, k), dtype=torch.uint8, device="cuda", generator=g)
+    c += (c >= 127).to(torch.uint8)
+    return c
+
+
+@pytest.mark.parametrize("side", ["lhs", "rhs"])
+def test_dense_operand_past_4gib(side):
+    """An operand of more than 4 GiB (266,240 rows of k = 16384): outputs
+    whose rows (LHS) or columns (RHS) lie past the first 4 GiB against the
+    oracle, and a few before."""
+    require_gpu()
+    big, small, k = 266240, (256 if side == "lhs" else 64), 16384
+    m, n = (big, small) if side == "lhs" else (small, big)
+    say(f"dense operand past 4 GiB side={side} m={m} n={n} k={k} {binding.fp8_gemm_describe(m, n, k)}")
+    kg, g = k // 128, torch.Generator(device="cuda").manual_seed(11)
+    a = _device_codes(m, k, seed=12)
+    b = _device_codes(n, k, seed=13)
+    sa = (0.5 + torch.rand(kg, ld_of(m), device="cuda", generator=g)) * 1e-2     # MN-major
+    sb = (0.5 + torch.rand((n + 127) // 128, kg, device="cuda", generator=g)) * 1e-2
+    out = torch.empty(m, n, dtype=torch.bfloat16, device="cuda")
+    nbytes = binding.fp8_gemm_workspace_bytes(m, n, k)
+    ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda") if nbytes else None
+    binding.fp8_gemm_nt(a, sa, b, sb, out, workspace=ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(14)
+    wrap = 2 ** 32 // k                                    # first row past 4 GiB
+    if side == "lhs":
+        # rows past 4 GiB (the last ones, random ones) and a few before
+        r_sel = np.unique(np.concatenate([np.arange(big - 16, big), rng.integers(wrap, big, 48),
+                                          rng.integers(0, wrap, 16)]))
+        ri = torch.from_numpy(r_sel).cuda()
+        qa, sa_rows = a[ri].cpu().numpy(), sa[:, ri].T.contiguous().cpu().numpy()
+        qb, sb_sub, c_sel = b.cpu().numpy(), sb.cpu().numpy(), np.arange(n)
+    else:
+        # whole 128-column blocks (each column takes its block's scale): the
+        # last two, two random ones past 4 GiB and one before
+        blocks = np.unique(np.concatenate([[big // 128 - 2, big // 128 - 1],
+                                           rng.integers(wrap // 128, big // 128, 2), rng.integers(0, wrap // 128, 1)]))
+        c_sel = (128 * blocks[:, None] + np.arange(128)).ravel()
+        ci = torch.from_numpy(c_sel).cuda()
+        qb, sb_sub = b[ci].cpu().numpy(), sb[torch.from_numpy(blocks).cuda()].cpu().numpy()
+        r_sel = np.arange(m)
+        qa, sa_rows = a.cpu().numpy(), sa[:, :m].T.contiguous().cpu().numpy()
+    rr, cc = (x.ravel() for x in np.meshgrid(np.arange(r_sel.size), np.arange(c_sel.size), indexing="ij"))
+    want = oracle.gemm_points(qa, sa_rows, qb, sb_sub, rr, cc)
+    got = out[torch.from_numpy(r_sel).cuda()][:, torch.from_numpy(c_sel).cuda()]
+    got = got.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).ravel()
+    assert_close(got, want, f"{side} past 4 GiB")

@@ -138,3 +138,16 @@ def test_masked_config3_sampled():
         r, c_ = sample_points(c, n, 300, seed=g)
         want = oracle.gemm_points(qa[g], sa[g], qb[g], sb[g], r, c_)
         assert_close(got[g][r, c_], want, f"group {g}")
+
+
+def test_masked_maximum_k():
+    """Masked kind at k = 65536 (512 K groups)."""
+    require_gpu()
+    G, max_m, n, k = 2, 64, 136, 65536
+    counts = np.array([37, 64], np.int32)
+    qa, sa, qb, sb = masked_case(G, max_m, n, k, counts, seed=9)
+    got = run_masked(qa, sa, qb, sb, counts)
+    for g in range(G):
+        c = int(counts[g])
+        assert_close(got[g, :c], oracle.gemm_nt(qa[g, :c], sa[g, :c], qb[g], sb[g]), f"group {g}")
+        assert np.all(got[g, c:] == SENTINEL)

@@ -4,11 +4,12 @@ kind for MoE decode).  Rows the kernel must not write keep the sentinel bit
 for bit; canary bands catch stores outside the output buffer."""
 import numpy as np
 import pytest
+import torch
 
 import oracle
-from fp8_block_scaled_04_amd import synth
-from _gpu import (SENTINEL, assert_close, contiguous_case, masked_case, require_gpu, run_contiguous,
-                  run_masked, sample_points, say)
+from fp8_block_scaled_04_amd import binding, synth
+from _gpu import (SENTINEL, assert_close, contiguous_case, dev, ld_of, masked_case, require_gpu, run_contiguous,
+                  run_masked, sa_mn_major, sample_points, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -151,3 +152,80 @@ def test_masked_maximum_k():
         c = int(counts[g])
         assert_close(got[g, :c], oracle.gemm_nt(qa[g, :c], sa[g, :c], qb[g], sb[g]), f"group {g}")
         assert np.all(got[g, c:] == SENTINEL)
+
+
+def _capture(fn):
+    """fn() captured into a HIP graph (after one warm-up on the capture stream)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
+def _bits(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def test_masked_graph_replays_read_new_counts():
+    """The masked counts are read on the device: one captured call, replayed
+    with different counts written into the same buffer between replays
+    (eager work in between), matches the oracle each time and leaves rows
+    past each count untouched."""
+    require_gpu()
+    G, max_m, n, k = 3, 192, 264, 768
+    schedules = [[192, 5, 64], [0, 130, 17], [64, 192, 0], [192, 5, 64]]
+    qa, sa, qb, sb = masked_case(G, max_m, n, k, np.max(schedules, axis=0), seed=21)
+    ld = ld_of(max_m)
+    a, s_ = dev(qa), dev(np.stack([sa_mn_major(sa[g], ld) for g in range(G)]))
+    b, t = dev(qb), dev(sb)
+    counts = torch.zeros(G, dtype=torch.int32, device="cuda")
+    out = torch.empty((G, max_m, n), dtype=torch.bfloat16, device="cuda")
+    graph = _capture(lambda: binding.fp8_grouped_gemm_masked(a, s_, b, t, out, counts))
+    for rep, cs in enumerate(schedules):
+        say(f"masked graph replay {rep} counts={cs}")
+        counts.copy_(torch.tensor(cs, dtype=torch.int32))
+        out.view(torch.int16).fill_(np.int16(SENTINEL))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = _bits(out)
+        for g, c in enumerate(cs):
+            if c:
+                assert_close(got[g, :c], oracle.gemm_nt(qa[g, :c], sa[g, :c], qb[g], sb[g]), f"replay {rep} group {g}")
+            assert np.all(got[g, c:] == SENTINEL), f"replay {rep}: group {g} wrote past its count"
+        binding.fp8_grouped_gemm_masked(a, s_, b, t, torch.empty_like(out), counts)   # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_contiguous_graph_replays_read_new_indices():
+    """The contiguous group indices are read on the device: one captured
+    call, replayed with a different row-block assignment each time (runs of
+    other lengths, a skipped block), matches the oracle each time."""
+    require_gpu()
+    n, k = 264, 512
+    qa, sa, qb, sb, _ = contiguous_case([256, 256, 128], n, k, seed=22)
+    M = qa.shape[0]
+    a, s_, b, t = dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb)
+    m_idx = torch.zeros(M, dtype=torch.int32, device="cuda")
+    out = torch.empty((M, n), dtype=torch.bfloat16, device="cuda")
+    graph = _capture(lambda: binding.fp8_grouped_gemm_contiguous(a, s_, b, t, out, m_idx))
+    for rep, blocks in enumerate([[0, 0, 1, 1, 2], [2, 0, 0, 0, 1], [1, -1, 2, 2, 2], [0, 1, 2, -1, -1]]):
+        say(f"contiguous graph replay {rep} blocks={blocks}")
+        rows = np.repeat(np.asarray(blocks, np.int32), 128)
+        m_idx.copy_(torch.from_numpy(rows))
+        out.view(torch.int16).fill_(np.int16(SENTINEL))
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = np.full((M, n), SENTINEL, np.uint16)
+        oracle.gemm_contiguous(qa, sa, qb, sb, rows, ref)
+        got = _bits(out)
+        valid = rows >= 0
+        assert_close(got[valid], ref[valid], f"replay {rep}")
+        assert np.all(got[~valid] == SENTINEL), f"replay {rep}: a skipped block was written"
+        binding.fp8_grouped_gemm_contiguous(a, s_, b, t, torch.empty_like(out), m_idx)   # eager work between replays
+        torch.cuda.synchronize()

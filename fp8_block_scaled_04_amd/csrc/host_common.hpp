@@ -62,8 +62,9 @@ inline int check_gemm_shape(int n, int k) {
   return FP8G_OK;
 }
 
+// (the kernels index a scale row with 32-bit ints)
 inline int check_ld(int64_t ld, int64_t rows) {
-  if (ld < rows || ld % 4 != 0 || ld < 4) return FP8G_EUNSUPPORTED;
+  if (ld < rows || ld % 4 != 0 || ld < 4 || ld > INT32_MAX) return FP8G_EUNSUPPORTED;
   return FP8G_OK;
 }
 

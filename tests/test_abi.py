@@ -65,6 +65,24 @@ def test_host_validation_paths(lib):
     assert b(None, 4, 6, None, None, None) == binding.FP8G_EUNSUPPORTED
 
 
+def test_scale_leading_dimension_limits(lib):
+    """ld below the rows, not a multiple of 4, or past 32 bits is refused
+    before anything is launched (the pointers are placeholders that are
+    never dereferenced: with no device present a launch could not happen
+    anyway, and with one this test does not run)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("placeholder pointers are only passed where no device exists")
+    p = ctypes.c_void_p(1 << 20)
+    g = lib.fp8_gemm_nt
+    for ld in (4, 6, 2 ** 31, 2 ** 32 + 8):
+        assert g(p, p, ld, p, p, p, 8, 8, 128, None, 0, None) == binding.FP8G_EUNSUPPORTED, ld
+    mk = lib.fp8_grouped_gemm_masked
+    assert mk(p, p, 2 ** 31 + 4, p, p, p, p, 2, 8, 8, 128, None, 0, None) == binding.FP8G_EUNSUPPORTED
+    c = lib.fp8_grouped_gemm_contiguous
+    assert c(p, p, 2 ** 31, p, p, p, p, 128, 8, 128, 2, None, 0, None) == binding.FP8G_EUNSUPPORTED
+
+
 def test_describe_reports_the_tile_choice(lib):
     """Host-only tile choice for a 256-CU device: 256 x 256 tiles for large
     M, narrow split tiles for small M."""

@@ -21,8 +21,8 @@
  *     (uint16); scales are FP32.  Every pointer must be 16-byte aligned.
  *   - KG = ceil(k / 128) and NB = ceil(n / 128).
  *   - LHS scales are stored MN-major: element (row r, K group g) lives at
- *     lhs_scales[g * lhs_scales_ld + r], with lhs_scales_ld >= rows and
- *     lhs_scales_ld % 4 == 0.  RHS scales are row-major [NB][KG].
+ *     lhs_scales[g * lhs_scales_ld + r], with rows <= lhs_scales_ld <
+ *     2^31 and lhs_scales_ld % 4 == 0.  RHS scales are row-major [NB][KG].
  *   - `stream` is a hipStream_t (NULL = the default stream).  Every call is
  *     asynchronous on that stream, never synchronises and never reads device
  *     data on the host, so calls may be captured into a HIP graph.
@@ -31,8 +31,8 @@
  *   - Errors that the host can check are reported before anything is
  *     launched: FP8G_EINVAL for null pointers, negative sizes or misaligned
  *     pointers; FP8G_EUNSUPPORTED for shapes outside this version's limits
- *     (k % 128 != 0, n % 8 != 0, contiguous m_total % 128 != 0, a bad
- *     scales ld); FP8G_ELAUNCH if the launch itself fails.  No C++ exception
+ *     (k % 128 != 0, k > 65536, n % 8 != 0, contiguous m_total % 128 != 0,
+ *     a bad scales ld); FP8G_ELAUNCH if the launch itself fails.  No C++ exception
  *     crosses this interface.
  *   - Zero-sized problems (m = 0, n = 0, num_groups = 0) succeed and launch
  *     nothing.

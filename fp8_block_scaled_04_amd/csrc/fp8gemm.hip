@@ -204,8 +204,10 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
   p.masked_m = masked_m;
   p.sa_ld = lhs_scales_ld;
   p.m = max_m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
-  // Row tiles past a group's count exit at once; the RHS tile of a group is
-  // read by each of its live row tiles (mostly from L2).
+  // The grid covers every possible unit; the kernel hands the live ones
+  // (row tiles below each group's count) to the first workgroups of each
+  // XCD and the rest exit at once.  The row tiles that share an RHS tile run
+  // together on one XCD, so after the first they read it from L2.
   p.tiles_m = int(cdiv(max_m, kMaskedShape.bm)); p.tiles_n = int(cdiv(n, kMaskedShape.bn)); p.splits = 1;
   p.groups_per_split = p.kg;
   const int64_t grid = int64_t(p.tiles_m) * p.tiles_n * num_groups;

@@ -260,6 +260,57 @@ __device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int
   nblocks = uniform(nblocks);
 }
 
+// Work units of the masked layout.  Group g has ceil(rows_g / BM) live row
+// tiles (rows_g = masked_m[g] clamped to [0, max_m]) for each of the tiles_n
+// column tiles; only these units have work.  They are numbered group by
+// group, column tile by column tile, row tile fastest, and XCD x takes the
+// x-th contiguous eighth of that numbering.  So the row tiles that share an
+// RHS tile run together on one XCD (the tile reaches that XCD's L2 once), a
+// group's LHS rows are fetched by the one or two XCDs its units fall on
+// (not by all eight), and every XCD gets the same number of live units.
+// Every wave derives the numbering from the (L2-resident) counts.  Returns
+// false for a workgroup past the live units of its XCD.
+template <int BM>
+__device__ __forceinline__ bool masked_unit(const int32_t* masked_m, int groups, int max_m, int tiles_n, int bid,
+                                            int& group, int& m_tile, int& n_tile) {
+  const int lane = threadIdx.x & (kWave - 1);
+  auto live_tiles = [&](int g) { return g < groups ? (min(max(masked_m[g], 0), max_m) + BM - 1) / BM : 0; };
+  auto inclusive_sum = [&](int v) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int t = __shfl_up(v, d, kWave);
+      if (lane >= d) v += t;
+    }
+    return v;
+  };
+  int total = 0;  // live units (< the grid size, so no overflow)
+  for (int g0 = 0; g0 < groups; g0 += kWave)
+    total += uniform(__shfl(inclusive_sum(live_tiles(g0 + lane) * tiles_n), kWave - 1, kWave));
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  const int per = total / kXcds, extra = total % kXcds;
+  if (slot >= per + (xcd < extra ? 1 : 0)) return false;
+  const int L = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
+  int base = 0;
+  for (int g0 = 0; g0 < groups; g0 += kWave) {
+    const int mt = live_tiles(g0 + lane);
+    const int u = mt * tiles_n;
+    const int incl = inclusive_sum(u);
+    const int first = base + incl - u;  // this lane's group's first unit
+    const unsigned long long who = __ballot(u > 0 && L >= first && L < first + u);
+    if (who) {
+      const int src = __ffsll(who) - 1;
+      const int mtg = uniform(__shfl(mt, src, kWave));
+      const int r = L - uniform(__shfl(first, src, kWave));
+      group = g0 + src;
+      m_tile = r % mtg;
+      n_tile = r / mtg;
+      return true;
+    }
+    base += uniform(__shfl(incl, kWave - 1, kWave));
+  }
+  return false;  // not reached: L < total
+}
+
 // KU consecutive K groups share one ring stage (one wait and one barrier),
 // and WK waves (dividing KU) may share each sub-tile, taking every WK-th
 // group of a stage; their partial tiles are added in LDS, in wave order,
@@ -347,10 +398,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     m_tile = first_m + in_band % rows_in_band;
     n_tile = in_band / rows_in_band;
   } else {
-    n_tile = bid % p.tiles_n;
-    bid /= p.tiles_n;
-    m_tile = bid % p.tiles_m;
-    group = bid / p.tiles_m;  // masked only
+    // (the grid spans every possible unit: groups x tiles_m x tiles_n)
+    if (!masked_unit<BM>(p.masked_m, int(gridDim.x) / (p.tiles_m * p.tiles_n), p.m, p.tiles_n, bid, group,
+                         m_tile, n_tile))
+      return;
   }
   int m0 = m_tile * BM;
   const int n0 = n_tile * BN;

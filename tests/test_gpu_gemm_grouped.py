@@ -95,6 +95,7 @@ def test_contiguous_config2_sampled():
     (3, 64, 136, 256, [0, 17, 64]),
     (4, 256, 264, 512, [1, 255, 256, 129]),
     (2, 300, 128, 384, [300, 33]),
+    (70, 64, 64, 128, [(7 * g) % 65 for g in range(70)]),  # more groups than lanes in a wave
 ])
 def test_masked_every_output(G, max_m, n, k, counts):
     require_gpu()

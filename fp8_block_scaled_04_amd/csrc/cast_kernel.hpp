@@ -68,17 +68,21 @@ __device__ __forceinline__ void load8(const uint16_t* x, float v[8]) {
   }
 }
 
-// Per-token-group cast.  Grid (ceil(m / 16), ceil(KG / G)), 256 threads: 16
-// lanes per (row, group), 8 consecutive elements per lane, G consecutive K
-// groups per workgroup with all of their loads issued before any is used.
-// Scales are written MN-major, scales[g * ld + row], 16 consecutive rows
-// per workgroup.
+// Per-token-group cast.  A 1-D grid of ceil(m / 16) * ceil(KG / G)
+// workgroups of 256 threads: 16 lanes per (row, group), 8 consecutive
+// elements per lane, G consecutive K groups per workgroup with all of their
+// loads issued before any is used.  Consecutive workgroups take consecutive
+// K groups of the same 16 rows, so the workgroups in flight read long runs
+// of each row (a column-stripe order, where they read one 128-element piece
+// of many rows, opens a new DRAM page for every piece).  Scales are written
+// MN-major, scales[g * ld + row], 16 consecutive rows per workgroup.
 template <typename T, int G, int FMT = kFmtE4M3>
 __global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x, int m, int k,
                                                          uint8_t* __restrict__ q,
                                                          float* __restrict__ scales, int64_t ld) {
-  const int row = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int g0 = blockIdx.y * G;
+  const unsigned gblocks = (unsigned(k) + kGroupK * G - 1) / (kGroupK * G);
+  const int row = int(blockIdx.x / gblocks) * 16 + (threadIdx.x >> 4);
+  const int g0 = int(blockIdx.x % gblocks) * G;
   float v[G][8];
 #pragma unroll
   for (int u = 0; u < G; ++u) {
@@ -106,15 +110,16 @@ __global__ void __launch_bounds__(256) cast_1x128_kernel(const T* __restrict__ x
   }
 }
 
-// 128 x 128 block cast.  Grid (NB, KG), 256 threads.  Each load instruction
-// of a wave covers two 512-byte row segments (32 lanes x 16 B); a thread
-// holds 16 rows x 4 columns.  k must be a multiple of 4.
+// 128 x 128 block cast.  A 1-D grid of NB * KG workgroups of 256 threads,
+// K blocks fastest (consecutive workgroups read along the same rows).  Each
+// load instruction of a wave covers two 512-byte row segments (32 lanes x
+// 16 B); a thread holds 16 rows x 4 columns.  k must be a multiple of 4.
 template <int FMT = kFmtE4M3>
 __global__ void __launch_bounds__(256) cast_128x128_kernel(const float* __restrict__ w, int n, int k,
                                                           uint8_t* __restrict__ q,
                                                           float* __restrict__ scales, int kg) {
   __shared__ float wave_max[4];
-  const int nb = blockIdx.x, g = blockIdx.y;
+  const int nb = int(blockIdx.x / unsigned(kg)), g = int(blockIdx.x % unsigned(kg));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = g * 128 + (lane & 31) * 4;
   const bool col_ok = col < k;

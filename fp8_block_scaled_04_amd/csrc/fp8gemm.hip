@@ -235,11 +235,13 @@ int fp8_cast_per_token_group_fmt(const void* x, int x_dtype, int q_format, int m
   if (!aligned16(x) || !aligned16(q) || !aligned16(scales)) return FP8G_EINVAL;
   if (scales_ld < m) return FP8G_EUNSUPPORTED;
   const int64_t kg = cdiv(k, 128);
-  if (kg > 65535) return FP8G_EUNSUPPORTED;
+  if (kg > 65535) return FP8G_EUNSUPPORTED;  // keeps the kernel's 32-bit column arithmetic in range
   // two K groups per workgroup once there are many (long rows of a large
   // activation): fewer, longer workgroups keep more loads in flight
   const bool pair = kg >= 64;
-  const dim3 grid(unsigned(cdiv(m, 16)), unsigned(pair ? cdiv(kg, 2) : kg));
+  const int64_t blocks = cdiv(m, 16) * (pair ? cdiv(kg, 2) : kg);
+  if (blocks > 0x7fffffff) return FP8G_EUNSUPPORTED;
+  const dim3 grid{unsigned(blocks)};
   auto s = static_cast<hipStream_t>(stream);
   if (q_format == FP8G_E5M2)
     launch_cast_1x128<fp8g::kFmtE5M2>(x, x_dtype, pair, grid, s, m, k, q, scales, scales_ld);
@@ -260,12 +262,13 @@ int fp8_cast_per_block_fmt(const float* w, int q_format, int n, int k, uint8_t* 
   if (!w || !q || !scales) return FP8G_EINVAL;
   if (!aligned16(w) || !aligned16(q) || !aligned16(scales)) return FP8G_EINVAL;
   const int64_t kg = cdiv(k, 128), nb = cdiv(n, 128);
-  if (kg > 65535 || nb > 0x7fffffff) return FP8G_EUNSUPPORTED;
+  if (kg > 65535 || nb * kg > 0x7fffffff) return FP8G_EUNSUPPORTED;
+  const dim3 grid{unsigned(nb * kg)};
   if (q_format == FP8G_E5M2)
-    hipLaunchKernelGGL(fp8g::cast_128x128_kernel<fp8g::kFmtE5M2>, dim3(unsigned(nb), unsigned(kg)), dim3(256), 0,
+    hipLaunchKernelGGL(fp8g::cast_128x128_kernel<fp8g::kFmtE5M2>, grid, dim3(256), 0,
                        static_cast<hipStream_t>(stream), w, n, k, q, scales, int(kg));
   else
-    hipLaunchKernelGGL(fp8g::cast_128x128_kernel<fp8g::kFmtE4M3>, dim3(unsigned(nb), unsigned(kg)), dim3(256), 0,
+    hipLaunchKernelGGL(fp8g::cast_128x128_kernel<fp8g::kFmtE4M3>, grid, dim3(256), 0,
                        static_cast<hipStream_t>(stream), w, n, k, q, scales, int(kg));
   return launched("block cast");
 }

@@ -145,12 +145,15 @@ int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales,
   p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
   p.tiles_m = c.tiles_m; p.tiles_n = c.tiles_n; p.splits = c.splits; p.groups_per_split = c.gps;
   const int64_t grid = int64_t(c.tiles_m) * c.tiles_n * c.splits;
+  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
   auto s = static_cast<hipStream_t>(stream);
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
                  c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
-  launch_dense_fmt(c.splits > 1, fmt, c.kind, p, grid, s);
-  return launched("gemm");
+  return launch_units(p, grid, [&](int64_t g) {
+    launch_dense_fmt(c.splits > 1, fmt, c.kind, p, g, s);
+    return launched("gemm");
+  });
 }
 
 int fp8_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
@@ -181,8 +184,10 @@ int fp8_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] contiguous M=%d n=%d k=%d G=%d grid<=%lld\n", m_total, n, k, num_groups,
                  (long long)grid);
-  launch_gemm<256, 256, 4, 2, 2, kContiguous, false>(p, grid, static_cast<hipStream_t>(stream));
-  return launched("contiguous gemm");
+  return launch_units(p, grid, [&](int64_t g) {
+    launch_gemm<256, 256, 4, 2, 2, kContiguous, false>(p, g, static_cast<hipStream_t>(stream));
+    return launched("contiguous gemm");
+  });
 }
 
 int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
@@ -215,8 +220,10 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
   if (log_enabled())
     std::fprintf(stderr, "[fp8gemm] masked G=%d max_m=%d n=%d k=%d grid=%lld\n", num_groups, max_m, n, k,
                  (long long)grid);
-  launch_gemm<64, 128, 1, 4, 3, kMasked, false>(p, grid, static_cast<hipStream_t>(stream));
-  return launched("masked gemm");
+  return launch_units(p, grid, [&](int64_t g) {
+    launch_gemm<64, 128, 1, 4, 3, kMasked, false>(p, g, static_cast<hipStream_t>(stream));
+    return launched("masked gemm");
+  });
 }
 
 int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k, uint8_t* q, float* scales,

@@ -51,6 +51,8 @@ struct GemmParams {
   int n, k, kg, nb;
   int tiles_m, tiles_n;
   int splits, groups_per_split;
+  int units;                 // work units of the call (tiles, or tiles x splits)
+  int unit_offset;           // first unit of this launch (launches under a CU limit take slices)
 };
 
 // Loads this lane's 32-byte K slice of one 16-row MFMA fragment from an LDS
@@ -368,14 +370,16 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   const int wm = (wave % (WAVES_M * WAVES_N)) / WAVES_N, wn = wave % WAVES_N;
 
   // ---- work unit ------------------------------------------------------
-  int bid = blockIdx.x;
+  // Unit blockIdx.x + p.unit_offset of p.units: a launch covers all units,
+  // or, under a CU limit, one of several consecutive slices of them.
+  const int bid = blockIdx.x + p.unit_offset;
   int split = 0;
   int n_tile, m_tile, group = 0;
   int tiles_m = p.tiles_m;
   [[maybe_unused]] ContigScan cs;
   if constexpr (MODE == kContiguous) {
-    // the grid is sized for the largest possible tile count; workgroups
-    // past the real count have nothing to do
+    // p.units is the largest possible tile count; units past the real count
+    // have nothing to do
     cs = contiguous_scan(p.m_indices, p.m / 128);
     tiles_m = cs.tiles;
     if (bid >= tiles_m * p.tiles_n) return;
@@ -386,7 +390,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     // groups of kGroupM M-tiles (M fastest), so the tiles an XCD runs at
     // once share a few A and B K-slices.  (A bijection, so correctness does
     // not depend on the dispatch order.)
-    const int total = MODE == kContiguous ? tiles_m * p.tiles_n : int(gridDim.x);
+    const int total = MODE == kContiguous ? tiles_m * p.tiles_n : p.units;
     const int xcd = bid % kXcds, slot = bid / kXcds;
     const int per = total / kXcds, extra = total % kXcds;
     int L = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
@@ -398,8 +402,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     m_tile = first_m + in_band % rows_in_band;
     n_tile = in_band / rows_in_band;
   } else {
-    // (the grid spans every possible unit: groups x tiles_m x tiles_n)
-    if (!masked_unit<BM>(p.masked_m, int(gridDim.x) / (p.tiles_m * p.tiles_n), p.m, p.tiles_n, bid, group,
+    // (p.units counts every possible unit: groups x tiles_m x tiles_n)
+    if (!masked_unit<BM>(p.masked_m, p.units / (p.tiles_m * p.tiles_n), p.m, p.tiles_n, bid, group,
                          m_tile, n_tile))
       return;
   }

@@ -33,6 +33,24 @@ inline int effective_cus() {
   return (lim > 0 && lim < d) ? lim : d;
 }
 
+// Launches a GEMM of `units` work units (one workgroup each): all in one
+// launch, or, while a CU limit is in force, in consecutive launches of at
+// most that many workgroups, so that at most that many CUs run the GEMM at
+// any time (later slices start when earlier ones have drained, in stream
+// order).  launch_one(grid) issues one launch of p with p.unit_offset set;
+// the first nonzero status it returns stops the sequence.
+template <typename Params, typename Launch>
+inline int launch_units(Params& p, int64_t units, Launch&& launch_one) {
+  p.units = int(units);
+  const int lim = g_cu_limit.load();
+  const int64_t step = (lim > 0 && lim < device_cus() && units > lim) ? lim : units;
+  for (int64_t off = 0; off < units; off += step) {
+    p.unit_offset = int(off);
+    if (const int st = launch_one(std::min(step, units - off))) return st;
+  }
+  return 0;
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }

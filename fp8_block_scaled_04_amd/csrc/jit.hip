@@ -490,13 +490,15 @@ int launch(const Program& prog, const GemmParams& p, int64_t grid, void* stream)
   if (const int st = get_kernel(prog, &fn)) return st;
   if (!fn) return FP8G_ELAUNCH;  // no device
   GemmParams local = p;
-  void* args[] = {&local};
-  if (hipModuleLaunchKernel(fn, unsigned(grid), 1, 1, unsigned(prog.threads), 1, 1, 0,
-                            static_cast<hipStream_t>(stream), args, nullptr) != hipSuccess) {
-    (void)hipGetLastError();
-    return FP8G_ELAUNCH;
-  }
-  return launched("jit gemm");
+  return launch_units(local, grid, [&](int64_t g) {
+    void* args[] = {&local};
+    if (hipModuleLaunchKernel(fn, unsigned(g), 1, 1, unsigned(prog.threads), 1, 1, 0,
+                              static_cast<hipStream_t>(stream), args, nullptr) != hipSuccess) {
+      (void)hipGetLastError();
+      return int(FP8G_ELAUNCH);
+    }
+    return launched("jit gemm");
+  });
 }
 
 int format_code(int lhs_format, int rhs_format, int* fmt) {

@@ -303,9 +303,13 @@ int fp8_moe_gather_rows(const uint16_t* y, int n, int y_rows, const int32_t* dst
  * (0 = never needed).  An upper bound; depends on the CU limit in force. */
 size_t fp8_gemm_workspace_bytes(int m, int n, int k, int num_groups);
 
-/* Limit the number of compute units the GEMM schedulers size their grids
- * for (the page's "SM resource control"), process-wide.  0 restores "all";
- * values above the device's count are clamped.  Returns the previous value. */
+/* Limit the number of compute units the GEMMs use (the page's "SM resource
+ * control"), process-wide.  Tile choices are made for that many CUs, and a
+ * GEMM with more workgroups than that runs as consecutive launches of at
+ * most that many workgroups on its stream, so at most that many CUs run it
+ * at any time and the rest stay free for concurrent work.  Results do not
+ * depend on the slicing.  0 restores "all"; values above the device's count
+ * are clamped.  Returns the previous value. */
 int fp8_set_num_cus(int num_cus);
 int fp8_get_num_cus(void);
 

@@ -123,16 +123,22 @@ def test_dense_split_and_unsplit_agree_and_are_deterministic():
     assert_close(c, ref, "unsplit")
 
 
-def test_dense_cu_limit_does_not_change_results():
+@pytest.mark.parametrize("m,n,k,cus", [(96, 512, 2048, 16), (64, 2112, 7168, 12), (1024, 2048, 1024, 5),
+                                      (300, 1000, 2048, 7)])
+def test_dense_cu_limit_does_not_change_results(m, n, k, cus):
+    """Under a CU limit the GEMM runs as consecutive launches of at most that
+    many workgroups (split-K partials and arrival counts carry across them);
+    every output still matches the oracle."""
     require_gpu()
-    qa, sa, qb, sb = dense_case(96, 512, 2048, seed=6)
+    qa, sa, qb, sb = dense_case(m, n, k, seed=6)
     ref = oracle.gemm_nt(qa, sa, qb, sb)
-    prev = binding.fp8_set_num_cus(16)
+    prev = binding.fp8_set_num_cus(cus)
     try:
+        say(f"dense m={m} n={n} k={k} limited to {cus} CUs: {binding.fp8_gemm_describe(m, n, k)}")
         got = run_dense(qa, sa, qb, sb)
     finally:
         binding.fp8_set_num_cus(prev)
-    assert_close(got, ref, "16 CUs")
+    assert_close(got, ref, f"{cus} CUs")
 
 
 def test_dense_scale_linearity_on_gpu():

@@ -230,3 +230,30 @@ def test_contiguous_graph_replays_read_new_indices():
         assert np.all(got[~valid] == SENTINEL), f"replay {rep}: a skipped block was written"
         binding.fp8_grouped_gemm_contiguous(a, s_, b, t, torch.empty_like(out), m_idx)   # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("cus", [7, 64])
+def test_grouped_cu_limit_gives_the_same_bits(cus):
+    """The grouped kinds keep their tile configuration under a CU limit and
+    run as consecutive launches of at most that many workgroups: the
+    results are bit-identical to the unlimited call, and rows outside the
+    valid ranges stay untouched."""
+    require_gpu()
+    sizes = [384, 128, 640]
+    qa, sa, qb, sb, m_idx = contiguous_case(sizes, 264, 512, seed=4)
+    counts = [0, 200, 37, 256, 64]
+    ma, msa, mb, msb = masked_case(5, 256, 136, 384, counts, seed=5)
+    want_c = run_contiguous(qa, sa, qb, sb, m_idx)
+    want_m = run_masked(ma, msa, mb, msb, counts)
+    prev = binding.fp8_set_num_cus(cus)
+    try:
+        say(f"grouped kinds limited to {cus} CUs")
+        got_c = run_contiguous(qa, sa, qb, sb, m_idx)
+        got_m = run_masked(ma, msa, mb, msb, counts)
+    finally:
+        binding.fp8_set_num_cus(prev)
+    assert np.array_equal(got_c, want_c)
+    assert np.array_equal(got_m, want_m)
+    for g, c in enumerate(counts):
+        assert np.all(got_m[g, c:] == SENTINEL)
+

@@ -177,3 +177,22 @@ def test_warmed_up_jit_call_replays_in_a_graph():
         assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref), f"replay {r}"
         binding.fp8_jit_gemm_nt(a, E4, s_, b, E4, t, eager, config=config, workspace=ws)   # eager work between
         torch.cuda.synchronize()
+
+
+def test_cu_limit_slices_give_the_same_bits():
+    """A runtime-specialised split-K GEMM under a CU limit (consecutive
+    launches of at most that many workgroups) gives the unlimited call's
+    bits: the configuration is fixed, and the split partials and arrival
+    counts carry across the launches."""
+    require_gpu()
+    config = dict(TILE_CONFIGS[0], specialize=0)
+    qa, sa, qb, sb = dense_case(200, 1032, 1664, seed=11)
+    want = run_jit(qa, sa, qb, sb, config=config)
+    prev = binding.fp8_set_num_cus(9)
+    try:
+        say("jit split-K limited to 9 CUs")
+        got = run_jit(qa, sa, qb, sb, config=config)
+    finally:
+        binding.fp8_set_num_cus(prev)
+    assert np.array_equal(got, want)
+

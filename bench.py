@@ -16,11 +16,11 @@ measured step time (cast included; the steps are bracketed by two events
 only).  Each timed step is a replay of a HIP graph holding that step's
 launches (one graph per rotation index), so the kernels run back to back;
 the same steps launched one call at a time from Python are timed as well
-(`ms_per_step_host_launched`).  Per-kernel durations come from a second phase that captures many
-launches of one kernel into a HIP graph and times its replays between two
-events on the same stream.  `roofline`
-describes the kernel that takes the most time: algorithmic FLOP (or bytes)
-per launch divided by its mean launch duration.  `cpu_baseline` times the CPU
+(`ms_per_step_host_launched`).  Per-kernel durations come from a second
+phase that captures many launches of one kernel into a HIP graph and times
+its replays between two events on the same stream.  `roofline` describes
+the kernel that takes the most time: algorithmic FLOP (or bytes) per launch
+divided by its mean launch duration.  `cpu_baseline` times the CPU
 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations

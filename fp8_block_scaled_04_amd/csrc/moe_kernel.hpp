@@ -136,6 +136,26 @@ __global__ void __launch_bounds__(256) moe_row_groups_kernel(const int32_t* __re
   }
 }
 
+// Copies `chunks` (> 0) 16-byte pieces with one wave.  Each lane issues 8
+// loads before it stores any of them: copied one piece at a time, every
+// store would wait for its own load, and a wave would keep only 1 KB in
+// flight.  Lanes past the end load the last piece again (unconditional
+// loads keep the 8 in flight together) and store nothing.
+__device__ __forceinline__ void wave_copy16(const v4i* __restrict__ src, v4i* __restrict__ dst, int chunks,
+                                            int lane) {
+  constexpr int U = 8;
+  for (int c0 = 0; c0 < chunks; c0 += U * kWave) {
+    v4i v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = src[min(c0 + u * kWave + lane, chunks - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave + lane;
+      if (c < chunks) dst[c] = v[u];
+    }
+  }
+}
+
 // Moves token t's E4M3 row and its KG scales to laid-out row dst[t].  One
 // wave per token, 16-byte copies (k % 16 == 0).  Scales: source MN-major
 // [KG][ld_in]; destination row d lives in group d / rpg at row d % rpg of
@@ -150,12 +170,14 @@ __global__ void __launch_bounds__(256) moe_scatter_kernel(const uint8_t* __restr
   if (t >= T) return;
   const int d = dst[t];
   if (d < 0 || d >= out_rows) return;
-  const v4i* src = reinterpret_cast<const v4i*>(q + int64_t(t) * k);
-  v4i* out = reinterpret_cast<v4i*>(q_out + int64_t(d) * k);
-  for (int c = lane; c < k / 16; c += kWave) out[c] = src[c];
   const int kg = (k + 127) / 128;
   float* so = scales_out + int64_t(d / rpg) * kg * ld_out + (d % rpg);
-  for (int g = lane; g < kg; g += kWave) so[int64_t(g) * ld_out] = scales[int64_t(g) * ld_in + t];
+  // the first 64 scales are loaded with the row
+  const float s0 = lane < kg ? scales[int64_t(lane) * ld_in + t] : 0.f;
+  wave_copy16(reinterpret_cast<const v4i*>(q + int64_t(t) * k), reinterpret_cast<v4i*>(q_out + int64_t(d) * k),
+              k / 16, lane);
+  if (lane < kg) so[int64_t(lane) * ld_out] = s0;
+  for (int g = kWave + lane; g < kg; g += kWave) so[int64_t(g) * ld_out] = scales[int64_t(g) * ld_in + t];
 }
 
 // out[t] = y[dst[t]] (BF16 rows, n % 8 == 0), zeros where dst[t] < 0.  One
@@ -172,8 +194,7 @@ __global__ void __launch_bounds__(256) moe_gather_kernel(const uint16_t* __restr
     for (int c = lane; c < n / 8; c += kWave) o[c] = v4i{0, 0, 0, 0};
     return;
   }
-  const v4i* src = reinterpret_cast<const v4i*>(y + int64_t(d) * n);
-  for (int c = lane; c < n / 8; c += kWave) o[c] = src[c];
+  wave_copy16(reinterpret_cast<const v4i*>(y + int64_t(d) * n), o, n / 8, lane);
 }
 
 }  // namespace fp8g

@@ -111,10 +111,13 @@ int fp8_moe_scatter_rows(const uint8_t* q, const float* scales, int64_t scales_l
     return FP8G_EINVAL;
   if (scales_ld < num_tokens || scales_out_ld < rows_per_group || out_rows % rows_per_group != 0)
     return FP8G_EINVAL;
-  const unsigned grid = unsigned(cdiv64(num_tokens, 4));
-  hipLaunchKernelGGL(fp8g::moe_scatter_kernel, dim3(grid), dim3(256), 0, static_cast<hipStream_t>(stream), q,
-                     scales, scales_ld, num_tokens, k, dst_row, rows_per_group, out_rows, q_out, scales_out,
-                     scales_out_ld);
+  // rows: four tokens per workgroup; scales: 256 tokens x kMoeScaleGroups K groups per workgroup
+  const int64_t row_blocks = cdiv64(num_tokens, 4);
+  const int64_t grid = row_blocks + cdiv64(num_tokens, 256) * cdiv64(cdiv64(k, 128), fp8g::kMoeScaleGroups);
+  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
+  hipLaunchKernelGGL(fp8g::moe_scatter_kernel, dim3(unsigned(grid)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     q, scales, scales_ld, num_tokens, k, dst_row, rows_per_group, out_rows, q_out, scales_out,
+                     scales_out_ld, int(row_blocks));
   return launched();
 }
 

@@ -156,28 +156,48 @@ __device__ __forceinline__ void wave_copy16(const v4i* __restrict__ src, v4i* __
   }
 }
 
-// Moves token t's E4M3 row and its KG scales to laid-out row dst[t].  One
-// wave per token, 16-byte copies (k % 16 == 0).  Scales: source MN-major
-// [KG][ld_in]; destination row d lives in group d / rpg at row d % rpg of
-// that group's MN-major [KG][ld_out] block.
+constexpr int kMoeScaleGroups = 8;  // K groups of scales per thread in the row scatter
+
+// Moves token t's E4M3 row and its KG scales to laid-out row dst[t].
+// Workgroups [0, row_blocks) move rows, one wave per token, 16-byte copies
+// (k % 16 == 0).  The rest move scales: one thread per token for
+// kMoeScaleGroups K groups, 256 consecutive tokens per workgroup, so the
+// reads of one K group's scales are coalesced (source MN-major
+// [KG][ld_in]) and so are the writes of tokens that land on consecutive
+// rows; destination row d lives in group d / rpg at row d % rpg of that
+// group's MN-major [KG][ld_out] block.
 __global__ void __launch_bounds__(256) moe_scatter_kernel(const uint8_t* __restrict__ q,
                                                           const float* __restrict__ scales, int64_t ld_in,
                                                           int T, int k, const int32_t* __restrict__ dst,
                                                           int rpg, int out_rows, uint8_t* __restrict__ q_out,
-                                                          float* __restrict__ scales_out, int64_t ld_out) {
+                                                          float* __restrict__ scales_out, int64_t ld_out,
+                                                          int row_blocks) {
+  if (int(blockIdx.x) >= row_blocks) {
+    // scale workgroup: 256 tokens x kMoeScaleGroups K groups
+    const int kg = (k + 127) / 128;
+    const int chunks = (kg + kMoeScaleGroups - 1) / kMoeScaleGroups;
+    const int b = blockIdx.x - row_blocks;
+    const int t = (b / chunks) * blockDim.x + threadIdx.x;
+    const int g0 = (b % chunks) * kMoeScaleGroups;
+    if (t >= T) return;
+    const int d = dst[t];
+    if (d < 0 || d >= out_rows) return;
+    float* so = scales_out + int64_t(d / rpg) * kg * ld_out + (d % rpg);
+    float v[kMoeScaleGroups];  // all loads in flight before the stores
+#pragma unroll
+    for (int u = 0; u < kMoeScaleGroups; ++u) v[u] = scales[int64_t(min(g0 + u, kg - 1)) * ld_in + t];
+#pragma unroll
+    for (int u = 0; u < kMoeScaleGroups; ++u)
+      if (g0 + u < kg) so[int64_t(g0 + u) * ld_out] = v[u];
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
   const int d = dst[t];
   if (d < 0 || d >= out_rows) return;
-  const int kg = (k + 127) / 128;
-  float* so = scales_out + int64_t(d / rpg) * kg * ld_out + (d % rpg);
-  // the first 64 scales are loaded with the row
-  const float s0 = lane < kg ? scales[int64_t(lane) * ld_in + t] : 0.f;
   wave_copy16(reinterpret_cast<const v4i*>(q + int64_t(t) * k), reinterpret_cast<v4i*>(q_out + int64_t(d) * k),
               k / 16, lane);
-  if (lane < kg) so[int64_t(lane) * ld_out] = s0;
-  for (int g = kWave + lane; g < kg; g += kWave) so[int64_t(g) * ld_out] = scales[int64_t(g) * ld_in + t];
 }
 
 // out[t] = y[dst[t]] (BF16 rows, n % 8 == 0), zeros where dst[t] < 0.  One

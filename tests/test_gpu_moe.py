@@ -63,11 +63,16 @@ def test_layout_rejects_too_few_rows():
     assert err.value.status == binding.FP8G_EINVAL
 
 
+# k = 8320: 65 K groups (several scale chunks per token, a partial last one)
+# and 520 16-byte pieces per row; n = 4160: 520 pieces per output row (more
+# than one batch of loads per lane in both copies)
+@pytest.mark.parametrize("k,n", [(384, 72), (8320, 4160)])
 @pytest.mark.parametrize("layout", ["contiguous", "masked"])
-def test_scatter_and_gather_bit_exact(layout):
+def test_scatter_and_gather_bit_exact(layout, k, n):
     require_gpu()
+    say(f"moe scatter/gather {layout} k={k} n={n}")
     rng = np.random.default_rng(3)
-    T, G, k, n = 777, 6, 384, 72
+    T, G = 777, 6
     kg = kg_of(k)
     e = routing(11, T, G)
     q = rng.integers(0, 256, (T, k), dtype=np.uint8)

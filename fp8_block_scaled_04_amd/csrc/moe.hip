@@ -66,6 +66,11 @@ int fp8_moe_layout_contiguous(const int32_t* expert_idx, int num_tokens, int num
   if (m_rows < need_rows) return FP8G_EINVAL;
   if (workspace_bytes < fp8_moe_layout_workspace_bytes(num_tokens, num_groups)) return FP8G_EINVAL;
   auto s = static_cast<hipStream_t>(stream);
+  if (num_tokens <= fp8g::kMoeSmallRounds * 1024) {  // one workgroup does it all
+    hipLaunchKernelGGL(fp8g::moe_layout_small_kernel<true>, dim3(1), dim3(1024), 0, s, expert_idx, num_tokens,
+                       num_groups, 0, counts, offsets, dst_row, m_indices, m_rows, nullptr);
+    return launched();
+  }
   auto* hist = static_cast<int32_t*>(workspace);
   count_and_scan(expert_idx, num_tokens, num_groups, hist, counts, offsets, nullptr, 0, s);
   const int64_t B = chunks(num_tokens);
@@ -90,6 +95,11 @@ int fp8_moe_layout_masked(const int32_t* expert_idx, int num_tokens, int num_gro
   if (int64_t(num_groups) * max_m > 0x7fffffff) return FP8G_EUNSUPPORTED;
   if (workspace_bytes < fp8_moe_layout_workspace_bytes(num_tokens, num_groups)) return FP8G_EINVAL;
   auto s = static_cast<hipStream_t>(stream);
+  if (num_tokens <= fp8g::kMoeSmallRounds * 1024) {  // one workgroup does it all
+    hipLaunchKernelGGL(fp8g::moe_layout_small_kernel<false>, dim3(1), dim3(1024), 0, s, expert_idx, num_tokens,
+                       num_groups, max_m, counts, nullptr, dst_row, nullptr, 0, masked_m);
+    return launched();
+  }
   auto* hist = static_cast<int32_t*>(workspace);
   count_and_scan(expert_idx, num_tokens, num_groups, hist, counts, nullptr, masked_m, max_m, s);
   const int64_t B = chunks(num_tokens);

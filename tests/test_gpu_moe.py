@@ -26,7 +26,10 @@ def routing(seed, T, G, unrouted=0.03, empty=True):
     return e.astype(np.int32)
 
 
-@pytest.mark.parametrize("T,G", [(1, 1), (1023, 8), (1024, 8), (1025, 64), (20000, 256), (70000, 1024)])
+# up to 4096 tokens one workgroup does the whole layout (experts matched by
+# ballot up to 64 experts, by lane shuffles above); past that, three passes
+@pytest.mark.parametrize("T,G", [(1, 1), (1023, 8), (1024, 8), (1025, 64), (4000, 200), (4096, 8), (4097, 8),
+                                 (16384, 8), (20000, 256), (70000, 1024)])
 def test_layout_contiguous_matches_oracle(T, G):
     require_gpu()
     say(f"moe layout contiguous T={T} G={G}")
@@ -43,7 +46,8 @@ def test_layout_contiguous_matches_oracle(T, G):
     assert np.array_equal(m_idx.cpu().numpy(), rm)
 
 
-@pytest.mark.parametrize("T,G,max_m", [(1, 1, 1), (300, 16, 8), (5000, 16, 256), (3000, 1000, 4)])
+@pytest.mark.parametrize("T,G,max_m", [(1, 1, 1), (300, 16, 8), (2048, 16, 256), (5000, 16, 256), (3000, 1000, 4),
+                                       (4096, 64, 300), (4097, 16, 2000), (16384, 64, 300)])
 def test_layout_masked_matches_oracle(T, G, max_m):
     require_gpu()
     say(f"moe layout masked T={T} G={G} max_m={max_m}")

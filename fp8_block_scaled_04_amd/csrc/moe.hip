@@ -73,14 +73,10 @@ int fp8_moe_layout_contiguous(const int32_t* expert_idx, int num_tokens, int num
   }
   auto* hist = static_cast<int32_t*>(workspace);
   count_and_scan(expert_idx, num_tokens, num_groups, hist, counts, offsets, nullptr, 0, s);
+  // destinations and m_indices in one launch (num_tokens > 4096 here, so B > 0)
   const int64_t B = chunks(num_tokens);
-  if (B > 0)
-    hipLaunchKernelGGL(fp8g::moe_dest_kernel<true>, dim3(unsigned(B)), dim3(1024), 0, s, expert_idx, num_tokens,
-                       num_groups, hist, offsets, 0, dst_row);
-  const unsigned grid = unsigned(std::min<int64_t>(cdiv64(m_rows, 256), 1024));
-  if (m_rows > 0)
-    hipLaunchKernelGGL(fp8g::moe_row_groups_kernel, dim3(grid), dim3(256), 0, s, offsets, num_groups, m_rows,
-                       m_indices);
+  hipLaunchKernelGGL(fp8g::moe_dest_kernel<true>, dim3(unsigned(B)), dim3(1024), 0, s, expert_idx, num_tokens,
+                     num_groups, hist, offsets, 0, dst_row, m_indices, m_rows);
   return launched();
 }
 
@@ -105,7 +101,7 @@ int fp8_moe_layout_masked(const int32_t* expert_idx, int num_tokens, int num_gro
   const int64_t B = chunks(num_tokens);
   if (B > 0)
     hipLaunchKernelGGL(fp8g::moe_dest_kernel<false>, dim3(unsigned(B)), dim3(1024), 0, s, expert_idx, num_tokens,
-                       num_groups, hist, nullptr, max_m, dst_row);
+                       num_groups, hist, nullptr, max_m, dst_row, nullptr, 0);
   return launched();
 }
 

@@ -83,18 +83,41 @@ __global__ void __launch_bounds__(1024) moe_scan_kernel(int32_t* __restrict__ hi
 // takes tokens [64 w, 64 w + 64) of the chunk.  rank = (tokens of the same
 // expert in earlier chunks) + (in earlier waves of this chunk) + (in earlier
 // lanes of this wave).
+//
+// Contiguous layout: the same workgroups also write m_indices[m_rows] (the
+// expert whose aligned block range holds each row, -1 past the last one),
+// row r by thread r of the grid-wide stride, from the offsets held in LDS.
 template <bool CONTIGUOUS>
 __global__ void __launch_bounds__(1024) moe_dest_kernel(const int32_t* __restrict__ expert, int T, int G,
                                                         const int32_t* __restrict__ hist,
                                                         const int32_t* __restrict__ offsets, int max_m,
-                                                        int32_t* __restrict__ dst) {
+                                                        int32_t* __restrict__ dst, int32_t* __restrict__ m_indices,
+                                                        int m_rows) {
   constexpr int NW = kMoeChunk / kWave;
   __shared__ int wave_cnt[NW][kMoeMaxGroups];
-  for (int i = threadIdx.x; i < NW * G; i += blockDim.x) wave_cnt[i / G][i % G] = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  __shared__ int off[CONTIGUOUS ? kMoeMaxGroups + 1 : 1];
   const int t = blockIdx.x * kMoeChunk + threadIdx.x;
-  const int e = t < T ? expert[t] : -1;
+  const int e = t < T ? expert[t] : -1;  // in flight while the counts are cleared
+  for (int i = threadIdx.x; i < NW * G; i += blockDim.x) wave_cnt[i / G][i % G] = 0;
+  if (CONTIGUOUS)
+    for (int g = threadIdx.x; g <= G; g += blockDim.x) off[g] = offsets[g];
+  __syncthreads();
+  if (CONTIGUOUS) {
+    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < m_rows; r += gridDim.x * blockDim.x) {
+      int v = -1;
+      if (r < off[G]) {
+        int lo = 0, hi = G - 1;  // last g with off[g] <= r
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off[mid] <= r) lo = mid;
+          else hi = mid - 1;
+        }
+        v = lo;
+      }
+      m_indices[r] = v;
+    }
+  }
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const bool ok = routed(e, G);
   int in_wave = 0;  // earlier lanes of this wave with the same expert
   for (int j = 0; j < kWave; ++j) {
@@ -110,30 +133,8 @@ __global__ void __launch_bounds__(1024) moe_dest_kernel(const int32_t* __restric
   }
   int rank = hist[int64_t(blockIdx.x) * G + e] + in_wave;
   for (int w = 0; w < wave; ++w) rank += wave_cnt[w][e];
-  if (CONTIGUOUS) dst[t] = offsets[e] + rank;
+  if (CONTIGUOUS) dst[t] = off[e] + rank;
   else dst[t] = rank < max_m ? e * max_m + rank : -1;
-}
-
-// m_indices[r] = the expert whose aligned block range holds r, -1 past the
-// last one.  Grid-stride over rows; the offsets are searched in LDS.
-__global__ void __launch_bounds__(256) moe_row_groups_kernel(const int32_t* __restrict__ offsets, int G, int rows,
-                                                             int32_t* __restrict__ m_indices) {
-  __shared__ int off[kMoeMaxGroups + 1];
-  for (int g = threadIdx.x; g <= G; g += blockDim.x) off[g] = offsets[g];
-  __syncthreads();
-  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < rows; r += gridDim.x * blockDim.x) {
-    int v = -1;
-    if (r < off[G]) {
-      int lo = 0, hi = G - 1;  // last g with off[g] <= r
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= r) lo = mid;
-        else hi = mid - 1;
-      }
-      v = lo;
-    }
-    m_indices[r] = v;
-  }
 }
 
 // Copies `chunks` (> 0) 16-byte pieces with one wave.  Each lane issues 8

@@ -57,10 +57,17 @@ __global__ void __launch_bounds__(1024) moe_scan_kernel(int32_t* __restrict__ hi
   const int g = threadIdx.x;
   int total = 0;
   if (g < G) {
-    for (int b = 0; b < B; ++b) {
-      const int c = hist[int64_t(b) * G + g];
-      hist[int64_t(b) * G + g] = total;
-      total += c;
+    constexpr int U = 16;  // chunks whose counts are loaded before any is rewritten
+    for (int b0 = 0; b0 < B; b0 += U) {
+      int c[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) c[u] = b0 + u < B ? hist[int64_t(b0 + u) * G + g] : 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (b0 + u < B) {
+          hist[int64_t(b0 + u) * G + g] = total;
+          total += c[u];
+        }
     }
     counts[g] = total;
     if (masked_m) masked_m[g] = min(total, max_m);
@@ -120,9 +127,17 @@ __global__ void __launch_bounds__(1024) moe_dest_kernel(const int32_t* __restric
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
   const bool ok = routed(e, G);
   int in_wave = 0;  // earlier lanes of this wave with the same expert
-  for (int j = 0; j < kWave; ++j) {
-    const int ej = __shfl(e, j, kWave);
-    if (j < lane && ej == e) ++in_wave;
+  if (G <= kWave) {  // one ballot per expert
+    const unsigned long long earlier = (1ull << lane) - 1;
+    for (int g = 0; g < G; ++g) {
+      const unsigned long long m = __ballot(e == g);
+      if (e == g) in_wave = __popcll(m & earlier);
+    }
+  } else {
+    for (int j = 0; j < kWave; ++j) {
+      const int ej = __shfl(e, j, kWave);
+      if (j < lane && ej == e) ++in_wave;
+    }
   }
   if (ok) atomicAdd(&wave_cnt[wave][e], 1);
   __syncthreads();

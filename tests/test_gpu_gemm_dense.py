@@ -243,6 +243,47 @@ def test_splitk_graph_replay_matches_eager():
         torch.cuda.synchronize()
 
 
+def test_cu_limit_slices_replay_in_a_graph():
+    """Under a CU limit a GEMM is several launches; captured into a HIP graph
+    and replayed with eager work in between, they reproduce the eager
+    result bit for bit (split-K partials and arrival counts included)."""
+    require_gpu()
+    m, n, k = 256, 512, 7168         # 128x64 tiles, 2 splits, 32 workgroups in slices of 24
+    qa, sa, qb, sb = dense_case(m, n, k, seed=13)
+    a, s_, b, t = _dense_dev(qa, sa, qb, sb)
+    prev = binding.fp8_set_num_cus(24)
+    try:
+        desc = binding.fp8_gemm_describe(m, n, k)
+        say(f"dense {m}x{n}x{k} limited to 24 CUs: {desc}")
+        grid = int(desc.split("grid=")[1])
+        assert grid > 24 and "splits=1 " not in desc, desc   # more than one slice, split-K
+        ws = torch.zeros(binding.fp8_gemm_workspace_bytes(m, n, k) // 4 + 1, dtype=torch.float32, device="cuda")
+        eager = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        binding.fp8_gemm_nt(a, s_, b, t, eager, workspace=ws)
+        torch.cuda.synchronize()
+        ref = eager.view(torch.int16).cpu().numpy()
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            binding.fp8_gemm_nt(a, s_, b, t, out, workspace=ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            binding.fp8_gemm_nt(a, s_, b, t, out, workspace=ws)
+        for rep in range(3):
+            out.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref), f"replay {rep}"
+            binding.fp8_gemm_nt(a, s_, b, t, eager, workspace=ws)
+            torch.cuda.synchronize()
+    finally:
+        binding.fp8_set_num_cus(prev)
+    assert_close(ref.view(np.uint16), oracle.gemm_nt(qa, sa, qb, sb), "24 CUs, graph")
+
+
 @pytest.mark.parametrize("m,n,k", [(16, 264, 65536), (200, 136, 65536)])
 def test_dense_maximum_k(m, n, k):
     """k = 65536, the largest the kernels take (512 K groups, every RHS scale

@@ -171,6 +171,105 @@ def _i32t(t, name):
     return _dev(t, name)
 
 
+# ---- extent checks ---------------------------------------------------------
+# The C ABI sees raw pointers only, so a tensor smaller than the sizes the
+# call derives from lhs / rhs would be read or written out of bounds on the
+# device.  Every tensor's shape and device is checked here, before the call.
+def _kg(k):
+    return (int(k) + 127) // 128
+
+
+def _want(t, name, shape):
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(int(v) for v in shape)}")
+
+
+def _want_dim(t, name, dim):
+    if t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions, got shape {tuple(t.shape)}")
+
+
+def _want_scales_mn(t, name, lead, rows):
+    """MN-major LHS scales: shape lead + (ld,) with ld >= rows."""
+    lead = tuple(int(v) for v in lead)
+    if t.dim() != len(lead) + 1 or tuple(t.shape[:-1]) != lead or t.shape[-1] < rows:
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {lead + ('ld',)} with ld >= {rows}")
+
+
+def _same_device(**tensors):
+    devs = {n: t.device for n, t in tensors.items() if t is not None}
+    first = next(iter(devs.values()))
+    for n, d in devs.items():
+        if d != first:
+            raise ValueError(f"{n} is on {d}, the other tensors on {first}")
+
+
+def _workspace_ok(ws, name="workspace"):
+    if ws is not None:
+        _dev(ws, name)
+    return ws
+
+
+def _check_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace):
+    _want_dim(lhs, "lhs", 2)
+    _want_dim(rhs, "rhs", 2)
+    m, k = lhs.shape
+    n = rhs.shape[0]
+    _want(rhs, "rhs", (n, k))
+    _want_scales_mn(lhs_scales, "lhs_scales", (_kg(k),), m)
+    _want(rhs_scales, "rhs_scales", (_kg(n), _kg(k)))
+    _want(out, "out", (m, n))
+    _workspace_ok(workspace)
+    _same_device(lhs=lhs, lhs_scales=lhs_scales, rhs=rhs, rhs_scales=rhs_scales, out=out, workspace=workspace)
+    return m, n, k
+
+
+def _check_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices):
+    _want_dim(lhs, "lhs", 2)
+    _want_dim(rhs, "rhs", 3)
+    M, k = lhs.shape
+    G, n = rhs.shape[0], rhs.shape[1]
+    _want(rhs, "rhs", (G, n, k))
+    _want_scales_mn(lhs_scales, "lhs_scales", (_kg(k),), M)
+    _want(rhs_scales, "rhs_scales", (G, _kg(n), _kg(k)))
+    _want(out, "out", (M, n))
+    _want(m_indices, "m_indices", (M,))
+    _same_device(lhs=lhs, lhs_scales=lhs_scales, rhs=rhs, rhs_scales=rhs_scales, out=out, m_indices=m_indices)
+    return M, n, k, G
+
+
+def _check_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m):
+    _want_dim(lhs, "lhs", 3)
+    _want_dim(rhs, "rhs", 3)
+    G, max_m, k = lhs.shape
+    n = rhs.shape[1]
+    _want(rhs, "rhs", (G, n, k))
+    _want_scales_mn(lhs_scales, "lhs_scales", (G, _kg(k)), max_m)
+    _want(rhs_scales, "rhs_scales", (G, _kg(n), _kg(k)))
+    _want(out, "out", (G, max_m, n))
+    _want(masked_m, "masked_m", (G,))
+    _same_device(lhs=lhs, lhs_scales=lhs_scales, rhs=rhs, rhs_scales=rhs_scales, out=out, masked_m=masked_m)
+    return G, max_m, n, k
+
+
+def _check_cast(x, q, scales):
+    _want_dim(x, "x", 2)
+    m, k = x.shape
+    _want(q, "q", (m, k))
+    _want_scales_mn(scales, "scales", (_kg(k),), m)
+    _same_device(x=x, q=q, scales=scales)
+    return m, k
+
+
+def _check_block_cast(w, q, scales):
+    _want_dim(w, "w", 2)
+    n, k = w.shape
+    _want(q, "q", (n, k))
+    _want(scales, "scales", (_kg(n), _kg(k)))
+    _same_device(w=w, q=q, scales=scales)
+    return n, k
+
+
 # ---- entry points ------------------------------------------------------------
 def fp8_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace=None, stream=None):
     """out[m][n] = block-scaled FP8 NT GEMM of lhs [m][k] and rhs [n][k].
@@ -178,8 +277,7 @@ def fp8_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace=None, stream=No
     lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out = _bf16(out, "out")
-    m, k = lhs.shape
-    n = rhs.shape[0]
+    m, n, k = _check_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().fp8_gemm_nt(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales), _p(out),
                            m, n, k, _p(workspace), ws_bytes, _stream(stream))
@@ -193,8 +291,7 @@ def fp8_gemm_nt_fmt(lhs, lhs_format, lhs_scales, rhs, rhs_format, rhs_scales, ou
     lhs, rhs = _codes(lhs, "lhs", lhs_format), _codes(rhs, "rhs", rhs_format)
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out = _bf16(out, "out")
-    m, k = lhs.shape
-    n = rhs.shape[0]
+    m, n, k = _check_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().fp8_gemm_nt_fmt(_p(lhs), lhs_format, _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), rhs_format,
                                _p(rhs_scales), _p(out), m, n, k, _p(workspace), ws_bytes, _stream(stream))
@@ -253,8 +350,7 @@ def fp8_jit_gemm_nt(lhs, lhs_format, lhs_scales, rhs, rhs_format, rhs_scales, ou
     lhs, rhs = _codes(lhs, "lhs", lhs_format), _codes(rhs, "rhs", rhs_format)
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out = _bf16(out, "out")
-    m, k = lhs.shape
-    n = rhs.shape[0]
+    m, n, k = _check_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().fp8_jit_gemm_nt(_p(lhs), lhs_format, _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), rhs_format,
                                _p(rhs_scales), _p(out), m, n, k, _cref(_config(config)), _p(workspace), ws_bytes,
@@ -267,8 +363,7 @@ def fp8_jit_grouped_gemm_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_ind
     lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out, m_indices = _bf16(out, "out"), _i32t(m_indices, "m_indices")
-    M, k = lhs.shape
-    G, n, _ = rhs.shape
+    M, n, k, G = _check_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices)
     st = lib().fp8_jit_grouped_gemm_contiguous(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs),
                                                _p(rhs_scales), _p(out), _p(m_indices), M, n, k, G,
                                                _cref(_config(config)), _stream(stream))
@@ -280,8 +375,7 @@ def fp8_jit_grouped_gemm_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m,
     lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out, masked_m = _bf16(out, "out"), _i32t(masked_m, "masked_m")
-    G, max_m, k = lhs.shape
-    n = rhs.shape[1]
+    G, max_m, n, k = _check_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m)
     st = lib().fp8_jit_grouped_gemm_masked(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales),
                                            _p(out), _p(masked_m), G, max_m, n, k, _cref(_config(config)),
                                            _stream(stream))
@@ -313,8 +407,7 @@ def fp8_grouped_gemm_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices
     lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out, m_indices = _bf16(out, "out"), _i32t(m_indices, "m_indices")
-    M, k = lhs.shape
-    G, n, _ = rhs.shape
+    M, n, k, G = _check_contiguous(lhs, lhs_scales, rhs, rhs_scales, out, m_indices)
     st = lib().fp8_grouped_gemm_contiguous(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales),
                                            _p(out), _p(m_indices), M, n, k, G, None, 0, _stream(stream))
     _check("fp8_grouped_gemm_contiguous", st)
@@ -327,8 +420,7 @@ def fp8_grouped_gemm_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m, str
     lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
     lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
     out, masked_m = _bf16(out, "out"), _i32t(masked_m, "masked_m")
-    G, max_m, k = lhs.shape
-    n = rhs.shape[1]
+    G, max_m, n, k = _check_masked(lhs, lhs_scales, rhs, rhs_scales, out, masked_m)
     st = lib().fp8_grouped_gemm_masked(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales),
                                        _p(out), _p(masked_m), G, max_m, n, k, None, 0, _stream(stream))
     _check("fp8_grouped_gemm_masked", st)
@@ -345,7 +437,7 @@ def fp8_cast_per_token_group(x, q, scales, stream=None):
     else:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
     q, scales = _codes(q, "q"), _f32(scales, "scales")
-    m, k = x.shape
+    m, k = _check_cast(x, q, scales)
     st = lib().fp8_cast_per_token_group(_p(x), dt, m, k, _p(q), _p(scales), scales.shape[-1], _stream(stream))
     _check("fp8_cast_per_token_group", st)
     return q, scales
@@ -362,7 +454,7 @@ def fp8_cast_per_token_group_fmt(x, q_format, q, scales, stream=None):
     else:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
     q, scales = _codes(q, "q", q_format), _f32(scales, "scales")
-    m, k = x.shape
+    m, k = _check_cast(x, q, scales)
     st = lib().fp8_cast_per_token_group_fmt(_p(x), dt, q_format, m, k, _p(q), _p(scales), scales.shape[-1],
                                             _stream(stream))
     _check("fp8_cast_per_token_group_fmt", st)
@@ -374,7 +466,7 @@ def fp8_cast_per_block_fmt(w, q_format, q, scales, stream=None):
     q_format = _fmt(q_format, "q_format")
     w = _f32(w, "w")
     q, scales = _codes(q, "q", q_format), _f32(scales, "scales")
-    n, k = w.shape
+    n, k = _check_block_cast(w, q, scales)
     st = lib().fp8_cast_per_block_fmt(_p(w), q_format, n, k, _p(q), _p(scales), _stream(stream))
     _check("fp8_cast_per_block_fmt", st)
     return q, scales
@@ -384,7 +476,7 @@ def fp8_cast_per_block(w, q, scales, stream=None):
     """w [n][k] float32 -> q [n][k] codes, scales [NB][KG] (128 x 128 blocks)."""
     w = _f32(w, "w")
     q, scales = _codes(q, "q"), _f32(scales, "scales")
-    n, k = w.shape
+    n, k = _check_block_cast(w, q, scales)
     st = lib().fp8_cast_per_block(_p(w), n, k, _p(q), _p(scales), _stream(stream))
     _check("fp8_cast_per_block", st)
     return q, scales
@@ -432,11 +524,15 @@ def fp8_moe_layout_contiguous(expert_idx, num_groups, m_rows=None, workspace=Non
     """Contiguous (prefill) layout of a routing.  Returns (counts [G],
     offsets [G+1], dst_row [T], m_indices [m_rows]) as int32 device tensors."""
     expert_idx = _i32t(expert_idx, "expert_idx")
+    _want_dim(expert_idx, "expert_idx", 1)
     T = expert_idx.numel()
     G = int(num_groups)
     if m_rows is None:
         m_rows = fp8_moe_contiguous_rows(T, G)
     dev = expert_idx.device
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        _same_device(expert_idx=expert_idx, workspace=workspace)
     counts = torch.empty(G, dtype=torch.int32, device=dev)
     offsets = torch.empty(G + 1, dtype=torch.int32, device=dev)
     dst = torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T]
@@ -454,9 +550,13 @@ def fp8_moe_layout_masked(expert_idx, num_groups, max_m, workspace=None, stream=
     """Masked (decode) layout of a routing.  Returns (counts [G], dst_row [T],
     masked_m [G]) as int32 device tensors."""
     expert_idx = _i32t(expert_idx, "expert_idx")
+    _want_dim(expert_idx, "expert_idx", 1)
     T = expert_idx.numel()
     G = int(num_groups)
     dev = expert_idx.device
+    if workspace is not None:
+        _dev(workspace, "workspace")
+        _same_device(expert_idx=expert_idx, workspace=workspace)
     counts = torch.empty(G, dtype=torch.int32, device=dev)
     masked_m = torch.empty(G, dtype=torch.int32, device=dev)
     dst = torch.empty(max(T, 1), dtype=torch.int32, device=dev)[:T]
@@ -476,10 +576,23 @@ def fp8_moe_scatter_rows(q, scales, dst_row, q_out, scales_out, rows_per_group=N
     q, q_out = _codes(q, "q"), _codes(q_out, "q_out")
     scales, scales_out = _f32(scales, "scales"), _f32(scales_out, "scales_out")
     dst_row = _i32t(dst_row, "dst_row")
+    _want_dim(q, "q", 2)
     T, k = q.shape
+    _want_scales_mn(scales, "scales", (_kg(k),), T)
+    _want(dst_row, "dst_row", (T,))
+    if q_out.dim() not in (2, 3) or q_out.shape[-1] != k:
+        raise ValueError(f"q_out has shape {tuple(q_out.shape)}, expected (rows, {k}) or (G, max_m, {k})")
     out_rows = q_out.numel() // k if k else 0
     if rows_per_group is None:
         rows_per_group = q_out.shape[-2] if q_out.dim() == 3 else out_rows
+    rows_per_group = int(rows_per_group)
+    # scales_out: one MN-major [KG][ld >= rows_per_group] block per group of rows
+    groups = -(-out_rows // rows_per_group) if rows_per_group > 0 else 0
+    if (scales_out.dim() < 2 or scales_out.shape[-2] != _kg(k) or scales_out.shape[-1] < rows_per_group
+            or scales_out.numel() < groups * _kg(k) * scales_out.shape[-1]):
+        raise ValueError(f"scales_out has shape {tuple(scales_out.shape)}, expected {groups} block(s) of "
+                         f"({_kg(k)}, ld >= {rows_per_group})")
+    _same_device(q=q, scales=scales, dst_row=dst_row, q_out=q_out, scales_out=scales_out)
     st = lib().fp8_moe_scatter_rows(_p(q), _p(scales), scales.shape[-1], T, k, _p(dst_row), int(rows_per_group),
                                     int(out_rows), _p(q_out), _p(scales_out), scales_out.shape[-1], _stream(stream))
     _check("fp8_moe_scatter_rows", st)
@@ -490,8 +603,14 @@ def fp8_moe_gather_rows(y, dst_row, out, stream=None):
     """out[t] = y[dst_row[t]] (bfloat16 rows), zeros where dst_row[t] < 0."""
     y, out = _bf16(y, "y"), _bf16(out, "out")
     dst_row = _i32t(dst_row, "dst_row")
+    _want_dim(dst_row, "dst_row", 1)
+    _want_dim(out, "out", 2)
     n = out.shape[-1]
+    _want(out, "out", (dst_row.numel(), n))
+    if y.dim() < 1 or y.shape[-1] != n:
+        raise ValueError(f"y has shape {tuple(y.shape)}, expected rows of {n} outputs")
     y_rows = y.numel() // n if n else 0
+    _same_device(y=y, dst_row=dst_row, out=out)
     st = lib().fp8_moe_gather_rows(_p(y), n, y_rows, _p(dst_row), dst_row.numel(), _p(out), _stream(stream))
     _check("fp8_moe_gather_rows", st)
     return out

@@ -20,30 +20,29 @@ void launch(const GemmParams& p, int64_t grid, hipStream_t s) {
 }
 
 template <bool SPLIT, int FMT>
-void launch_kind(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+int launch_kind(int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
   switch (kind) {
-    case kS128N64: launch<128, 64, 2, 2, 4, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kF64N32: launch<64, 32, 4, 1, 4, SPLIT, 2, 1, FMT>(p, grid, s); break;
-    case kF64N64: launch<64, 64, 2, 2, 4, SPLIT, 2, 2, FMT>(p, grid, s); break;
-    case kF64N128: launch<64, 128, 4, 2, 4, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    case kF128N128: launch<128, 128, 4, 2, 3, SPLIT, 1, 1, FMT>(p, grid, s); break;
-    default:
-      // the 256 x 256 tile cannot stage a split partial (dense_config never
-      // asks for it)
-      if constexpr (!SPLIT) launch<256, 256, 4, 2, 2, false, 1, 1, FMT>(p, grid, s);
-      break;
+    case kS128N64: launch<128, 64, 2, 2, 4, SPLIT, 1, 1, FMT>(p, grid, s); return FP8G_OK;
+    case kF64N32: launch<64, 32, 4, 1, 4, SPLIT, 2, 1, FMT>(p, grid, s); return FP8G_OK;
+    case kF64N64: launch<64, 64, 2, 2, 4, SPLIT, 2, 2, FMT>(p, grid, s); return FP8G_OK;
+    case kF64N128: launch<64, 128, 4, 2, 4, SPLIT, 1, 1, FMT>(p, grid, s); return FP8G_OK;
+    case kF128N128: launch<128, 128, 4, 2, 3, SPLIT, 1, 1, FMT>(p, grid, s); return FP8G_OK;
+    case kBig:
+      // the 256 x 256 tile cannot stage a split partial in its ring
+      if constexpr (SPLIT) return FP8G_EUNSUPPORTED;
+      else { launch<256, 256, 4, 2, 2, false, 1, 1, FMT>(p, grid, s); return FP8G_OK; }
+    default: return FP8G_EUNSUPPORTED;
   }
 }
 
 }  // namespace
 
 template <int FMT>
-void launch_dense_kind(bool split, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
-  if (split) launch_kind<true, FMT>(kind, p, grid, s);
-  else launch_kind<false, FMT>(kind, p, grid, s);
+int launch_dense_kind(bool split, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+  return split ? launch_kind<true, FMT>(kind, p, grid, s) : launch_kind<false, FMT>(kind, p, grid, s);
 }
 
-template void launch_dense_kind<FP8G_DENSE_FMT>(bool, int, const GemmParams&, int64_t, hipStream_t);
+template int launch_dense_kind<FP8G_DENSE_FMT>(bool, int, const GemmParams&, int64_t, hipStream_t);
 
 }  // namespace host
 }  // namespace fp8g

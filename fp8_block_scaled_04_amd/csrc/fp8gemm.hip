@@ -36,12 +36,12 @@ void launch_gemm(const GemmParams& p, int64_t grid, hipStream_t s) {
 
 // The dense GEMM kernels are instantiated in dense_launch.hip, one object per
 // operand-format pair (FMT: bit 0 = LHS in E5M2, bit 1 = RHS in E5M2).
-void launch_dense_fmt(bool split, int fmt, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
+int launch_dense_fmt(bool split, int fmt, int kind, const GemmParams& p, int64_t grid, hipStream_t s) {
   switch (fmt) {
-    case 1: fp8g::host::launch_dense_kind<1>(split, kind, p, grid, s); break;
-    case 2: fp8g::host::launch_dense_kind<2>(split, kind, p, grid, s); break;
-    case 3: fp8g::host::launch_dense_kind<3>(split, kind, p, grid, s); break;
-    default: fp8g::host::launch_dense_kind<0>(split, kind, p, grid, s); break;
+    case 1: return fp8g::host::launch_dense_kind<1>(split, kind, p, grid, s);
+    case 2: return fp8g::host::launch_dense_kind<2>(split, kind, p, grid, s);
+    case 3: return fp8g::host::launch_dense_kind<3>(split, kind, p, grid, s);
+    default: return fp8g::host::launch_dense_kind<0>(split, kind, p, grid, s);
   }
 }
 
@@ -151,7 +151,7 @@ int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales,
     std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
                  c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
   return launch_units(p, grid, [&](int64_t g) {
-    launch_dense_fmt(c.splits > 1, fmt, c.kind, p, g, s);
+    if (const int st = launch_dense_fmt(c.splits > 1, fmt, c.kind, p, g, s)) return st;  // before any launch
     return launched("gemm");
   });
 }

@@ -187,8 +187,13 @@ inline DenseConfig dense_config(int m, int n, int k, bool allow_split) {
     if (allow_split && can_split && 2 * tiles <= cus + tiles / 2)
       splits = int(std::min<int64_t>(kg, (cus + tiles / 2) / tiles));
   }
-  if (!allow_split || !can_split) splits = 1;
-  splits = std::max(1, std::min(std::min(kg, kMaxSplits), env_int("FP8G_SPLITS", splits)));
+  if (allow_split && can_split) {
+    // FP8G_SPLITS overrides the split count (tuning only); it never turns
+    // split-K on where the workspace or the tile cannot take it
+    splits = std::max(1, std::min(std::min(kg, kMaxSplits), env_int("FP8G_SPLITS", splits)));
+  } else {
+    splits = 1;
+  }
   c.gps = int(cdiv(kg, splits));
   c.splits = int(cdiv(kg, c.gps));
   return c;

@@ -162,25 +162,66 @@ void parallel_rows(int64_t rows, int nthreads, F&& body) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ---- integer form of the codes --------------------------------------------
+// Every finite E4M3 value is an integer multiple of 2^-9 (the smallest
+// subnormal) and every finite E5M2 value a multiple of 2^-16, so code c has
+// value mant[c] * 2^-q with an integer mant[c] (|mant| <= 448 * 2^9 for E4M3,
+// <= 57344 * 2^16 < 2^32 for E5M2).  nonfinite[c] marks NaN / infinity codes.
+struct IntTable {
+  int64_t mant[256];
+  uint8_t nonfinite[256];
+  int q;
+  explicit IntTable(int fmt) {
+    q = fmt == kE5M2 ? 16 : 9;
+    for (unsigned c = 0; c < 256; ++c) {
+      const double v = table(fmt).v[c];
+      nonfinite[c] = std::isfinite(v) ? 0 : 1;
+      mant[c] = std::isfinite(v) ? int64_t(std::ldexp(v, q)) : 0;  // exact
+    }
+  }
+};
+const IntTable& int_table(int fmt) {
+  static const IntTable t4(kE4M3), t5(kE5M2);
+  return fmt == kE5M2 ? t5 : t4;
+}
+
 // ---- one output element of the block-scaled GEMM ---------------------------
 // [DG-day3] "Core features" and "Source walk-through" part 3:
 //   D[i][j] = sum_g (sa[i][g] * sb[j/128][g]) * S_g(i, j),
 //   S_g(i, j) = sum_{t in K group g} dec(A[i][t]) * dec(B[j][t]).
-// Each S_g is exact in FP64 (every E4M3 value is a multiple of 2^-9 below
-// 2^9, so a 128-term sum of products is a multiple of 2^-18 below 2^43).
-// (With E5M2 operands the values are multiples of 2^-16 below 2^16, so the
-// products and their 128-term sums stay exact as well.)
+// S_g is summed exactly on the integer mantissas (a 128-term sum of products
+// below 2^64 each fits in 128 bits) and rounded once to FP64.  For two E4M3
+// operands that rounding is exact: the sum is an integer below 2^43 times
+// 2^-18.  With an E5M2 operand the exact sum can need up to about 71
+// significant bits (products are multiples of 2^-32 up to 2^31.6), so S_g is
+// the correctly rounded FP64 value of the exact sum.  A NaN or infinite code
+// in the group makes S_g the plain FP64 sum of the decoded products, so the
+// NaN or infinity propagates as IEEE arithmetic gives it.
+double group_sum(const uint8_t* a, const uint8_t* b, int64_t len, int a_fmt, int b_fmt) {
+  const IntTable& ia = int_table(a_fmt);
+  const IntTable& ib = int_table(b_fmt);
+  __int128 s = 0;
+  unsigned bad = 0;
+  for (int64_t t = 0; t < len; ++t) {
+    s += __int128(ia.mant[a[t]]) * __int128(ib.mant[b[t]]);
+    bad |= unsigned(ia.nonfinite[a[t]] | ib.nonfinite[b[t]]);
+  }
+  if (!bad) return std::ldexp(double(s), -(ia.q + ib.q));  // one rounding (int128 -> double is RNE)
+  const double* va = table(a_fmt).v;
+  const double* vb = table(b_fmt).v;
+  double d = 0.0;
+  for (int64_t t = 0; t < len; ++t) d += va[a[t]] * vb[b[t]];
+  return d;
+}
+
 double gemm_element(const uint8_t* a_row, const float* sa_row,
                     const uint8_t* b_row, const float* sb_row, int64_t k,
                     int a_fmt = kE4M3, int b_fmt = kE4M3) {
-  const double* va = table(a_fmt).v;
-  const double* vb = table(b_fmt).v;
   const int64_t kg = ceil_div(k, 128);
   double acc = 0.0;
   for (int64_t g = 0; g < kg; ++g) {
     const int64_t t0 = g * 128, t1 = std::min<int64_t>(t0 + 128, k);
-    double s = 0.0;
-    for (int64_t t = t0; t < t1; ++t) s += va[a_row[t]] * vb[b_row[t]];
+    const double s = group_sum(a_row + t0, b_row + t0, t1 - t0, a_fmt, b_fmt);
     acc += (double(sa_row[g]) * double(sb_row[g])) * s;
   }
   return acc;

@@ -144,14 +144,3 @@ def run_masked(qa, sa, qb, sb, counts):
     binding.fp8_grouped_gemm_masked(dev(qa), dev(sa_dev), dev(qb), dev(sb), out.view,
                                     dev(np.asarray(counts, np.int32)))
     return out.result()
-
-
-def sample_points(rows, n, count, seed):
-    """Output coordinates that cover every 16-row and 16-column sub-tile
-    boundary class plus the last row/column, then random ones."""
-    rng = np.random.default_rng(seed)
-    r = list(range(min(rows, 20))) + list(range(max(0, rows - 20), rows))
-    c = list(range(min(n, 20))) + list(range(max(0, n - 20), n))
-    rr = np.concatenate([np.array(r), rng.integers(0, rows, count)])
-    cc = np.concatenate([np.array(c)[rng.integers(0, len(c), len(r))], rng.integers(0, n, count)])
-    return rr.astype(np.int64), cc.astype(np.int64)

@@ -148,3 +148,19 @@ def test_oracle_and_gpu_path_share_nothing():
             text = open(os.path.join(ROOT, "oracle", f)).read()
             assert "fp8_block_scaled_04_amd" not in text, f
             assert "fp8gemm" not in text and "hip" not in text.lower().replace("ship", ""), f
+
+
+def test_split_override_only_where_split_k_can_run(lib, monkeypatch):
+    """FP8G_SPLITS (a tuning override) changes the split count only where
+    split-K is possible: never for the 256 x 256 tile, whose ring cannot
+    stage a split partial, and never without a workspace."""
+    if binding.fp8_get_num_cus() != 256:
+        pytest.skip("the expectations are for a 256-CU device (or no device)")
+    monkeypatch.setenv("FP8G_SPLITS", "4")
+    d = binding.fp8_gemm_describe
+    for shape in [(4096, 7168, 16384), (8192, 8192, 8192)]:
+        desc = d(*shape)
+        assert desc.startswith("tile=256x256 ") and "splits=1 " in desc, desc
+        assert binding.fp8_gemm_workspace_bytes(*shape) == 0
+    assert "splits=4 " in d(64, 2112, 7168)          # the override itself works where split-K runs
+    assert binding.fp8_gemm_workspace_bytes(64, 2112, 7168) > 0

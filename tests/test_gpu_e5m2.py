@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from fp8_block_scaled_04_amd import binding, synth
-from _gpu import Guarded, assert_close, dev, kg_of, ld_of, require_gpu, sa_mn_major, sample_points, say
+from _gpu import Guarded, assert_close, dev, kg_of, ld_of, require_gpu, sa_mn_major, say
 
 pytestmark = pytest.mark.gpu
 
@@ -138,17 +138,16 @@ def test_gemm_format_pairs_every_output(m, n, k, a_fmt, b_fmt):
     assert_close(got, ref, f"lhs {a_fmt} rhs {b_fmt} {m}x{n}x{k}")
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("a_fmt,b_fmt", PAIRS)
-def test_gemm_format_pairs_large_sampled(a_fmt, b_fmt):
-    """The dominant shape (4096 x 7168 x 16384), checked on sampled outputs."""
+def test_gemm_format_pairs_large(a_fmt, b_fmt):
+    """The dominant shape (4096 x 7168 x 16384), every output."""
     require_gpu()
     m, n, k = 4096, 7168, 16384
-    say(f"gemm fmt lhs={a_fmt} rhs={b_fmt} sampled {m}x{n}x{k}")
+    say(f"gemm fmt lhs={a_fmt} rhs={b_fmt} {m}x{n}x{k} (every output)")
     qa, sa, qb, sb = case(m, n, k, a_fmt, b_fmt, seed=11)
     got = run(qa, sa, qb, sb, a_fmt, b_fmt)
-    rows, cols = sample_points(m, n, 2000, seed=5)
-    ref = oracle.gemm_points(qa, sa, qb, sb, rows, cols, a_fmt=a_fmt, b_fmt=b_fmt)
-    assert_close(got[rows, cols], ref, "sampled")
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb, a_fmt=a_fmt, b_fmt=b_fmt), f"lhs {a_fmt} rhs {b_fmt}")
 
 
 def test_gemm_e4m3_pair_matches_plain_entry_point():

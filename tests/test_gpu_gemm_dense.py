@@ -2,17 +2,16 @@
 ("DeepSeek open-source week, day 3: DeepGEMM": "Basic usage" operands and
 scales, "Core features" two-level accumulation, BF16 output).
 
-Every output is compared at small and medium sizes; at the full workload
-sizes, sampled outputs are computed one by one by the oracle.  Output
-buffers carry canary bands, so stray stores fail the test."""
+Every output of every workload shape is compared with the oracle, the rms
+of the tolerance taken over all of the call's outputs.  Output buffers
+carry canary bands, so stray stores fail the test."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from fp8_block_scaled_04_amd import binding
-from _gpu import (assert_close, dense_case, dev, ld_of, require_gpu, run_dense, sa_mn_major, sample_points,
-                  say, Guarded)
+from _gpu import assert_close, dense_case, dev, ld_of, require_gpu, run_dense, sa_mn_major, say, Guarded
 
 pytestmark = pytest.mark.gpu
 
@@ -56,16 +55,17 @@ def test_dense_small_m_tile_families_every_output(shape, tile, split):
         assert np.array_equal(got, run_dense(qa, sa, qb, sb)), "split-K result not deterministic"
 
 
+@pytest.mark.timeout(300)
 def test_dense_k_tail_regression_shape():
     """The K-tail failure shape of the jianying88 practice article (§6.1):
-    M = N = 6144, K = 1280, checked on sampled outputs."""
+    M = N = 6144, K = 1280, every output."""
     require_gpu()
     m = n = 6144
     k = 1280
+    say(f"dense k-tail shape {m}x{n}x{k} (every output)")
     qa, sa, qb, sb = dense_case(m, n, k, seed=61)
     got = run_dense(qa, sa, qb, sb)
-    r, c = sample_points(m, n, 3000, seed=1)
-    assert_close(got[r, c], oracle.gemm_points(qa, sa, qb, sb, r, c), "6144x6144x1280")
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), "6144x6144x1280")
 
 
 def test_dense_config0_full():
@@ -83,31 +83,29 @@ def test_dense_config0_full():
 NK = [(4096, 7168), (7168, 2048), (24576, 1536), (7168, 16384)]
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("m", [64, 128, 4096])
 @pytest.mark.parametrize("n,k", NK)
 def test_dense_config1_sweep(m, n, k):
-    """The m x (n, k) sweep: m <= 128 every output, m = 4096 sampled."""
+    """The m x (n, k) sweep, every output."""
     require_gpu()
-    say(f"dense sweep m={m} n={n} k={k}")
+    say(f"dense sweep m={m} n={n} k={k} (every output)")
     qa, sa, qb, sb = dense_case(m, n, k, seed=0)
     got = run_dense(qa, sa, qb, sb)
-    if m <= 128:
-        ref = oracle.gemm_nt(qa, sa, qb, sb)
-        assert_close(got, ref, f"{m}x{n}x{k}")
-    else:
-        r, c = sample_points(m, n, 4000, seed=m + n)
-        assert_close(got[r, c], oracle.gemm_points(qa, sa, qb, sb, r, c), f"{m}x{n}x{k} sampled")
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("m,n,k", [(8192, 8192, 8192), (16384, 7168, 16384)])
-def test_dense_config4_outliers_sampled(m, n, k):
-    """Large compute-bound shapes with 1% of elements scaled by 50."""
+def test_dense_config4_outliers(m, n, k):
+    """Large compute-bound shapes with 1% of the elements of both operands
+    scaled by 50 before quantisation: every output."""
     require_gpu()
-    say(f"dense large m={m} n={n} k={k} (outliers, sampled)")
+    say(f"dense large m={m} n={n} k={k} (outliers, every output)")
     qa, sa, qb, sb = dense_case(m, n, k, seed=0, outliers=True)
     got = run_dense(qa, sa, qb, sb)
-    r, c = sample_points(m, n, 3000, seed=4)
-    assert_close(got[r, c], oracle.gemm_points(qa, sa, qb, sb, r, c), f"{m}x{n}x{k} sampled")
+    say(f"  GPU done; oracle over {m * n * k / 1e12:.2f} T MAC")
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"{m}x{n}x{k}")
 
 
 def test_dense_split_and_unsplit_agree_and_are_deterministic():
@@ -319,11 +317,12 @@ def _device_codes(rows, k, seed):
     return c
 
 
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("side", ["lhs", "rhs"])
 def test_dense_operand_past_4gib(side):
-    """An operand of more than 4 GiB (266,240 rows of k = 16384): outputs
-    whose rows (LHS) or columns (RHS) lie past the first 4 GiB against the
-    oracle, and a few before."""
+    """An operand of more than 4 GiB (266,240 rows of k = 16384), LHS or RHS:
+    every output against the oracle, so rows (LHS) or columns (RHS) on both
+    sides of the first 4 GiB are covered."""
     require_gpu()
     big, small, k = 266240, (256 if side == "lhs" else 64), 16384
     m, n = (big, small) if side == "lhs" else (small, big)
@@ -338,27 +337,9 @@ def test_dense_operand_past_4gib(side):
     ws = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda") if nbytes else None
     binding.fp8_gemm_nt(a, sa, b, sb, out, workspace=ws)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(14)
-    wrap = 2 ** 32 // k                                    # first row past 4 GiB
-    if side == "lhs":
-        # rows past 4 GiB (the last ones, random ones) and a few before
-        r_sel = np.unique(np.concatenate([np.arange(big - 16, big), rng.integers(wrap, big, 48),
-                                          rng.integers(0, wrap, 16)]))
-        ri = torch.from_numpy(r_sel).cuda()
-        qa, sa_rows = a[ri].cpu().numpy(), sa[:, ri].T.contiguous().cpu().numpy()
-        qb, sb_sub, c_sel = b.cpu().numpy(), sb.cpu().numpy(), np.arange(n)
-    else:
-        # whole 128-column blocks (each column takes its block's scale): the
-        # last two, two random ones past 4 GiB and one before
-        blocks = np.unique(np.concatenate([[big // 128 - 2, big // 128 - 1],
-                                           rng.integers(wrap // 128, big // 128, 2), rng.integers(0, wrap // 128, 1)]))
-        c_sel = (128 * blocks[:, None] + np.arange(128)).ravel()
-        ci = torch.from_numpy(c_sel).cuda()
-        qb, sb_sub = b[ci].cpu().numpy(), sb[torch.from_numpy(blocks).cuda()].cpu().numpy()
-        r_sel = np.arange(m)
-        qa, sa_rows = a.cpu().numpy(), sa[:, :m].T.contiguous().cpu().numpy()
-    rr, cc = (x.ravel() for x in np.meshgrid(np.arange(r_sel.size), np.arange(c_sel.size), indexing="ij"))
-    want = oracle.gemm_points(qa, sa_rows, qb, sb_sub, rr, cc)
-    got = out[torch.from_numpy(r_sel).cuda()][:, torch.from_numpy(c_sel).cuda()]
-    got = got.contiguous().view(torch.int16).cpu().numpy().view(np.uint16).ravel()
-    assert_close(got, want, f"{side} past 4 GiB")
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    qa, qb = a.cpu().numpy(), b.cpu().numpy()
+    del a, b
+    sa_rows, sb_h = sa[:, :m].T.contiguous().cpu().numpy(), sb.cpu().numpy()
+    say(f"  GPU done; oracle over {m * n * k / 1e12:.2f} T MAC")
+    assert_close(got, oracle.gemm_nt(qa, sa_rows, qb, sb_h), f"{side} past 4 GiB")

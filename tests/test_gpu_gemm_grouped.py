@@ -9,7 +9,7 @@ import torch
 import oracle
 from fp8_block_scaled_04_amd import binding, synth
 from _gpu import (SENTINEL, assert_close, contiguous_case, dev, ld_of, masked_case, require_gpu, run_contiguous,
-                  run_masked, sa_mn_major, sample_points, say)
+                  run_masked, sa_mn_major, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -76,19 +76,17 @@ def test_contiguous_tiling_patterns(pattern):
     assert_close(got[valid], ref[valid], f"contiguous {pattern}")
 
 
-def test_contiguous_config2_sampled():
-    """G=8, n=4096, k=7168, m_g = 128 * U{4..32} (seed 0)."""
+@pytest.mark.timeout(300)
+def test_contiguous_config2():
+    """G=8, n=4096, k=7168, m_g = 128 * U{4..32} (seed 0): every output."""
     require_gpu()
     sizes = synth.contiguous_group_sizes(8, seed=0)
-    say(f"contiguous G=8 sizes={list(sizes)} n=4096 k=7168 (sampled)")
+    say(f"contiguous G=8 sizes={list(sizes)} n=4096 k=7168 (every output)")
     qa, sa, qb, sb, m_idx = contiguous_case(sizes, 4096, 7168, seed=0)
     got = run_contiguous(qa, sa, qb, sb, m_idx)
-    starts = np.concatenate([[0], np.cumsum(sizes)])
-    for g in range(8):
-        lo, hi = starts[g], starts[g + 1]
-        r, c = sample_points(hi - lo, 4096, 500, seed=g)
-        want = oracle.gemm_points(qa[lo:hi], sa[lo:hi], qb[g], sb[g], r, c)
-        assert_close(got[lo + r, c], want, f"expert {g}")
+    ref = np.full(got.shape, SENTINEL, np.uint16)
+    oracle.gemm_contiguous(qa, sa, qb, sb, m_idx, ref)
+    assert_close(got, ref, "contiguous G=8")
 
 
 @pytest.mark.parametrize("G,max_m,n,k,counts", [
@@ -122,24 +120,25 @@ def test_masked_counts_are_clamped():
     assert_close(got[0], ref[0], "clamped count")
 
 
-def test_masked_config3_sampled():
+@pytest.mark.timeout(300)
+def test_masked_config3():
     """G=16, max_m=256, n=4096, k=7168, counts ~ U[0, 256] (seed 0); rows
     past each count hold random bytes (NaN codes and NaN/Inf scales
-    included) and must neither affect nor receive output."""
+    included) and must neither affect nor receive output.  Every valid
+    output is compared, the rms over all of them (all groups)."""
     require_gpu()
     G, max_m, n, k = 16, 256, 4096, 7168
     counts = synth.masked_counts(G, max_m, seed=0)
-    say(f"masked G=16 max_m=256 n=4096 k=7168 counts={list(counts)} (sampled)")
+    say(f"masked G=16 max_m=256 n=4096 k=7168 counts={list(counts)} (every output)")
     qa, sa, qb, sb = masked_case(G, max_m, n, k, counts, seed=0)
     got = run_masked(qa, sa, qb, sb, counts)
+    ref = np.full((G, max_m, n), SENTINEL, np.uint16)
+    oracle.gemm_masked(qa, sa, qb, sb, np.asarray(counts, np.int32), ref)
     for g in range(G):
-        c = int(counts[g])
-        assert np.all(got[g, c:] == SENTINEL), f"group {g} wrote past its count"
-        if c == 0:
-            continue
-        r, c_ = sample_points(c, n, 300, seed=g)
-        want = oracle.gemm_points(qa[g], sa[g], qb[g], sb[g], r, c_)
-        assert_close(got[g][r, c_], want, f"group {g}")
+        assert np.all(got[g, int(counts[g]):] == SENTINEL), f"group {g} wrote past its count"
+    valid = np.concatenate([got[g, :int(c)].ravel() for g, c in enumerate(counts)])
+    want = np.concatenate([ref[g, :int(c)].ravel() for g, c in enumerate(counts)])
+    assert_close(valid, want, "masked G=16")
 
 
 def test_masked_maximum_k():

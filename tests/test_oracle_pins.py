@@ -639,3 +639,44 @@ def test_e5m2_gemm_bruteforce_rational(a_fmt, b_fmt):
             tot = sum(va[i][t] * Fraction(float(sa[i, t // 128])) * vb[j][t] * Fraction(float(sb[j // 128, t // 128]))
                       for t in range(k))
             assert out[i, j] == bf16_nearest_exact(tot), (i, j)
+
+
+def test_group_sum_is_exact_where_fp64_summation_is_not():
+    """E5M2 products span 2^-32 .. 2^31.6, so a group sum can need ~71
+    significant bits: summed left to right in FP64, 2^30 + 2^-32 - 2^30
+    loses the small term.  The oracle sums each K group exactly and rounds
+    once, so it returns 2^-32 (as exact rational arithmetic does)."""
+    k = 128
+    A = np.zeros((1, k), np.uint8)
+    B = np.zeros((1, k), np.uint8)
+    big, tiny, neg_big = 0x78, 0x01, 0xF8            # E5M2: 2^15, 2^-16, -2^15
+    A[0, :3] = [big, tiny, neg_big]
+    B[0, :3] = [big, tiny, big]
+    one = np.ones((1, 1), np.float32)
+    dec = oracle.fp8_table(oracle.E5M2)
+    assert dec[big] == 2.0 ** 15 and dec[tiny] == 2.0 ** -16 and dec[neg_big] == -2.0 ** 15
+    out, pre = oracle.gemm_nt(A, one, B, one, want_pre=True, a_fmt=oracle.E5M2, b_fmt=oracle.E5M2)
+    assert pre[0, 0] == 2.0 ** -32
+    assert out[0, 0] == oracle.bf16_rne(2.0 ** -32)
+    # the same cancellation spread over a mixed-format pair (E4M3 x E5M2):
+    # 448 * 2^15, then 2^-9 * 2^-16, then -448 * 2^15
+    A4 = np.zeros((1, k), np.uint8)
+    A4[0, :3] = [0x7E, 0x01, 0xFE]                    # E4M3: 448, 2^-9, -448
+    out, pre = oracle.gemm_nt(A4, one, B, one, want_pre=True, a_fmt=oracle.E4M3, b_fmt=oracle.E5M2)
+    assert pre[0, 0] == 2.0 ** -25
+
+
+def test_group_sum_propagates_nonfinite_codes():
+    """A NaN code (E4M3 0x7F) or an infinity (E5M2 0x7C) in a group makes
+    that output NaN or infinite, as IEEE arithmetic on the decoded values."""
+    k = 256
+    A = np.full((2, k), 0x38, np.uint8)               # 1.0
+    B = np.full((1, k), 0x38, np.uint8)
+    A[0, 5] = 0x7F
+    one = np.ones((2, 2), np.float32)
+    _, pre = oracle.gemm_nt(A, one, B, one[:1], want_pre=True)
+    assert np.isnan(pre[0, 0]) and pre[1, 0] == 256.0
+    A5 = np.full((1, k), 0x3C, np.uint8)              # E5M2 1.0
+    A5[0, 200] = 0x7C                                 # +inf
+    _, pre = oracle.gemm_nt(A5, one[:1], B, one[:1], want_pre=True, a_fmt=oracle.E5M2, b_fmt=oracle.E4M3)
+    assert pre[0, 0] == np.inf

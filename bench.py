@@ -92,6 +92,8 @@ def main():
                     help="time host-launched steps only (no HIP graph replay of the step)")
     ap.add_argument("--no-grouped", action="store_true",
                     help="skip the grouped-GEMM measurements (MoE prefill and decode configurations)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other dense workloads (m=64 n=2112 k=7168; the large outlier shapes)")
     args = ap.parse_args()
     if args.digest:
         print(kernel_source_digest())
@@ -120,51 +122,9 @@ def main():
 
     # ---- inputs: generate, upload, quantise weights, rotate ----------------
     t0 = time.time()
-    host = {}
-    cases = []
-    for (m, n, k) in shapes:
-        key = (m, k)
-        if key not in host:
-            x = synth.normal_f32(0, synth.S_LHS, (m, k))
-            if outliers:
-                x = synth.with_outliers(x, 0, synth.S_OUT_LHS)
-            host[key] = x
-        if (n, k) not in host:
-            w = synth.normal_f32(0, synth.S_RHS, (n, k))
-            if outliers:
-                w = synth.with_outliers(w, 0, synth.S_OUT_RHS)
-            host[(n, k)] = w
-    print(f"[bench] inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-
-    for (m, n, k) in shapes:
-        kg, nb = math.ceil(k / 128), math.ceil(n / 128)
-        ld = max(4, (m + 3) // 4 * 4)
-        x_d = torch.from_numpy(host[(m, k)]).cuda()
-        w_d = torch.from_numpy(host[(n, k)]).cuda()
-        qb0 = torch.empty((n, k), dtype=torch.uint8, device="cuda")
-        sb0 = torch.empty((nb, kg), dtype=torch.float32, device="cuda")
-        binding.fp8_cast_per_block(w_d, qb0, sb0)
-        del w_d
-        foot = 4 * m * k + m * k + kg * ld * 4 + n * k + nb * kg * 4 + 2 * m * n
-        reps = int(min(64, max(1, math.ceil(ROTATE_BYTES / foot))))
-        ws_bytes = binding.fp8_gemm_workspace_bytes(m, n, k)
-        ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device="cuda") if ws_bytes else None
-        sets = []
-        for r in range(reps):
-            sets.append(dict(
-                x=x_d if r == 0 else x_d.clone(),
-                q=torch.empty((m, k), dtype=torch.uint8, device="cuda"),
-                s=torch.empty((kg, ld), dtype=torch.float32, device="cuda"),
-                qb=qb0 if r == 0 else qb0.clone(),
-                sb=sb0 if r == 0 else sb0.clone(),
-                out=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
-            ))
-        flop, nbytes = algorithmic(m, n, k)
-        cases.append(dict(m=m, n=n, k=k, sets=sets, ws=ws, flop=flop, bytes=nbytes,
-                          cast_bytes=cast_bytes(m, k)))
-    torch.cuda.synchronize()
-    print(f"[bench] device buffers ready ({torch.cuda.memory_allocated() / 2**30:.1f} GiB)",
-          file=sys.stderr, flush=True)
+    host, cases = build_cases(shapes, outliers)
+    print(f"[bench] inputs ready in {time.time() - t0:.1f}s ({torch.cuda.memory_allocated() / 2**30:.1f} GiB "
+          f"on the device)", file=sys.stderr, flush=True)
 
     def cast(c, b, st=stream):
         binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=st)
@@ -227,24 +187,7 @@ def main():
 
     # ---- per-kernel launch durations -------------------------------------
     total_flop = sum(c["flop"] for c in cases)
-    by_shape = []
-    for c in cases:
-        reps = max(10, min(200, int(2e4 / max(1.0, c["flop"] / 1e9))))
-        batches = replay_mean_ms(torch, stream, lambda b, st: gemm(c, b, st), c["sets"], reps, 3)
-        gemm_ms = float(np.median(batches))
-        cast_ms = float(np.median(replay_mean_ms(torch, stream, lambda b, st: cast(c, b, st), c["sets"], reps, 1)))
-        gemm_all = batches
-        c["gemm_ms"], c["cast_ms"] = gemm_ms, cast_ms
-        c["gemm_mean_ms"] = float(np.mean(batches))
-        tflops = c["flop"] / (gemm_ms * 1e-3) / 1e12
-        gbs = c["bytes"] / (gemm_ms * 1e-3) / 1e9
-        bound = "mfma" if c["flop"] / c["bytes"] >= RIDGE else "hbm"
-        frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
-        by_shape.append(dict(m=c["m"], n=c["n"], k=c["k"], gemm_us=round(gemm_ms * 1e3, 2),
-                             gemm_us_min_max=[round(min(gemm_all) * 1e3, 2), round(max(gemm_all) * 1e3, 2)],
-                             cast_us=round(cast_ms * 1e3, 2), tflops=round(tflops, 1), gbs=round(gbs, 1),
-                             bound=bound, frac=round(frac, 4),
-                             cast_gbs=round(c["cast_bytes"] / (cast_ms * 1e-3) / 1e9, 1)))
+    by_shape = [time_gemm_case(torch, stream, c) for c in cases]
     dom = max(cases, key=lambda c: c["gemm_ms"])
     dom_bound = "mfma" if dom["flop"] / dom["bytes"] >= RIDGE else "hbm"
     # mean launch duration (HIP events on the launch stream), as rocprofv3 averages
@@ -294,18 +237,127 @@ def main():
 
     if not args.no_jit:
         result["jit"] = jit_measurements(torch, stream, cases)
+    sweep_shapes = list(shapes)
+    del cases, graphs
+    torch.cuda.empty_cache()
     if not args.no_grouped and not args.shape:
-        del cases, sets
-        torch.cuda.empty_cache()
         result["grouped"] = grouped_measurements(stream)
+    if not args.no_configs and not args.shape:
+        torch.cuda.empty_cache()
+        result["dense_configs"] = dense_config_measurements(torch, stream)
     if not args.no_extra and not args.shape:
         torch.cuda.empty_cache()
         result["moe_layout"] = moe_measurements(stream)
         torch.cuda.empty_cache()
         result["formats"] = format_measurements(stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(shapes, host, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(sweep_shapes, host, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def build_cases(shapes, outliers):
+    """Seeded N(0, 1) fp32 activations and weights for every shape (1% of
+    the elements of both operands x50 when `outliers`), uploaded; weights
+    quantised once by the 128x128 block cast; every buffer rotated over
+    enough copies that >= 1 GiB is touched between two uses of one copy."""
+    import torch
+    from fp8_block_scaled_04_amd import binding, synth
+    host = {}
+    for (m, n, k) in shapes:
+        if (m, k) not in host:
+            x = synth.normal_f32(0, synth.S_LHS, (m, k))
+            if outliers:
+                x = synth.with_outliers(x, 0, synth.S_OUT_LHS)
+            host[(m, k)] = x
+        if (n, k) not in host:
+            w = synth.normal_f32(0, synth.S_RHS, (n, k))
+            if outliers:
+                w = synth.with_outliers(w, 0, synth.S_OUT_RHS)
+            host[(n, k)] = w
+    cases = []
+    for (m, n, k) in shapes:
+        kg, nb = math.ceil(k / 128), math.ceil(n / 128)
+        ld = max(4, (m + 3) // 4 * 4)
+        x_d = torch.from_numpy(host[(m, k)]).cuda()
+        w_d = torch.from_numpy(host[(n, k)]).cuda()
+        qb0 = torch.empty((n, k), dtype=torch.uint8, device="cuda")
+        sb0 = torch.empty((nb, kg), dtype=torch.float32, device="cuda")
+        binding.fp8_cast_per_block(w_d, qb0, sb0)
+        del w_d
+        foot = 4 * m * k + m * k + kg * ld * 4 + n * k + nb * kg * 4 + 2 * m * n
+        reps = int(min(64, max(1, math.ceil(ROTATE_BYTES / foot))))
+        ws_bytes = binding.fp8_gemm_workspace_bytes(m, n, k)
+        ws = torch.empty(max(1, ws_bytes // 4), dtype=torch.float32, device="cuda") if ws_bytes else None
+        sets = []
+        for r in range(reps):
+            sets.append(dict(
+                x=x_d if r == 0 else x_d.clone(),
+                q=torch.empty((m, k), dtype=torch.uint8, device="cuda"),
+                s=torch.empty((kg, ld), dtype=torch.float32, device="cuda"),
+                qb=qb0 if r == 0 else qb0.clone(),
+                sb=sb0 if r == 0 else sb0.clone(),
+                out=torch.empty((m, n), dtype=torch.bfloat16, device="cuda"),
+            ))
+        flop, nbytes = algorithmic(m, n, k)
+        cases.append(dict(m=m, n=n, k=k, sets=sets, ws=ws, flop=flop, bytes=nbytes,
+                          cast_bytes=cast_bytes(m, k)))
+    torch.cuda.synchronize()
+    return host, cases
+
+
+def time_gemm_case(torch, stream, c):
+    """Median and mean launch duration of the case's GEMM (graph replays of
+    rotated launches), its cast's median, and the roofline record."""
+    from fp8_block_scaled_04_amd import binding
+
+    def gemm(b, st):
+        binding.fp8_gemm_nt(b["q"], b["s"], b["qb"], b["sb"], b["out"], workspace=c["ws"], stream=st)
+
+    def cast(b, st):
+        binding.fp8_cast_per_token_group(b["x"], b["q"], b["s"], stream=st)
+
+    reps = max(10, min(200, int(2e4 / max(1.0, c["flop"] / 1e9))))
+    batches = replay_mean_ms(torch, stream, gemm, c["sets"], reps, 3)
+    gemm_ms = float(np.median(batches))
+    cast_ms = float(np.median(replay_mean_ms(torch, stream, cast, c["sets"], reps, 1)))
+    c["gemm_ms"], c["cast_ms"], c["gemm_mean_ms"] = gemm_ms, cast_ms, float(np.mean(batches))
+    tflops = c["flop"] / (gemm_ms * 1e-3) / 1e12
+    gbs = c["bytes"] / (gemm_ms * 1e-3) / 1e9
+    bound = "mfma" if c["flop"] / c["bytes"] >= RIDGE else "hbm"
+    frac = tflops / PEAK_FP8_TFLOPS if bound == "mfma" else gbs / PEAK_HBM_GBS
+    return dict(m=c["m"], n=c["n"], k=c["k"], gemm_us=round(gemm_ms * 1e3, 2),
+                mean_launch_us=round(c["gemm_mean_ms"] * 1e3, 2),
+                gemm_us_min_max=[round(min(batches) * 1e3, 2), round(max(batches) * 1e3, 2)],
+                cast_us=round(cast_ms * 1e3, 2), tflops=round(tflops, 1), gbs=round(gbs, 1),
+                bound=bound, frac=round(frac, 4), cast_gbs=round(c["cast_bytes"] / (cast_ms * 1e-3) / 1e9, 1))
+
+
+# The other dense workloads, measured beside the metric's sweep: the small
+# case (m=64, n=2112, k=7168) and the large compute-bound shapes with 1% of
+# the elements of both operands scaled by 50.
+DENSE_CONFIGS = [
+    ("config0", "dense m=64 n=2112 k=7168, N(0,1), seed 0", [(64, 2112, 7168)], False),
+    ("config4", "dense m=n=k=8192 and m=16384 n=7168 k=16384, N(0,1) with 1% of elements x50, seed 0",
+     [(8192, 8192, 8192), (16384, 7168, 16384)], True),
+]
+
+
+def dense_config_measurements(torch, stream):
+    out = {}
+    for name, desc, shapes, outliers in DENSE_CONFIGS:
+        t0 = time.time()
+        _, cases = build_cases(shapes, outliers)
+        recs = []
+        for c in cases:
+            rec = time_gemm_case(torch, stream, c)
+            rec["rotated_sets"] = len(c["sets"])
+            recs.append(rec)
+            print(f"[bench] {name} {c['m']}x{c['n']}x{c['k']}: {rec['gemm_us']} us, {rec['tflops']} TFLOP/s, "
+                  f"{rec['gbs']} GB/s ({rec['bound']} {rec['frac']})", file=sys.stderr, flush=True)
+        out[name] = dict(workload=desc, shapes=recs, seconds=round(time.time() - t0, 1))
+        del cases
+        torch.cuda.empty_cache()
+    return out
 
 
 def jit_measurements(torch, stream, cases):
@@ -661,11 +713,31 @@ def copy_calibration(nbytes, steps):
     print(json.dumps({"copy_bytes": nbytes, "launches": steps}), flush=True)
 
 
+def host_description():
+    """Threads, nproc and CPU model of the machine the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return dict(nproc=os.cpu_count(), affinity=affinity, cpu_model=model)
+
+
 def cpu_baseline(shapes, host, target_s):
-    """The CPU oracle (as it stands) on a bounded sample of the same workload:
-    the first r rows of every shape (cast + GEMM), all host threads, with r
-    sized from a short calibration so the sample takes about `target_s`
-    seconds.  Scaled to the metric's unit (TFLOP/s of GEMM work)."""
+    """The CPU oracle (as it stands) on the metric's workload: every row of
+    every shape (cast of the fp32 activations + GEMM), on all the threads the
+    oracle uses, scaled to the metric's unit (TFLOP/s of GEMM work).  Only
+    if a short calibration predicts more than 3 x `target_s` seconds is the
+    first r rows of every shape timed instead, r sized to about `target_s`
+    seconds (and the sample says so)."""
     import oracle
     threads = oracle.hardware_threads()
     wq = {}
@@ -686,20 +758,21 @@ def cpu_baseline(shapes, host, target_s):
             flop += 2.0 * r * n * k
         return flop, t
 
-    # calibrate twice: tiny samples are dominated by fixed costs
     mmax = max(m for m, _, _ in shapes)
-    rows = 8
-    for _ in range(2):
-        _, t0 = run(rows)
-        nxt = int(max(8, min(mmax, rows * 0.5 * target_s / max(t0, 1e-3))))
-        if nxt <= rows:
-            break
-        rows = nxt
-    rows = int(max(8, min(mmax, rows * target_s / max(run(rows)[1], 1e-3))))
+    total_flop = sum(2.0 * m * n * k for m, n, k in shapes)
+    cal_flop, cal_t = run(32)                      # calibration: 32 rows of every shape
+    predicted = cal_t * total_flop / cal_flop
+    if predicted <= 3 * target_s:
+        rows, what = mmax, "the whole workload: every row of every shape"
+    else:
+        rows = int(max(32, min(mmax, 32 * target_s / max(cal_t, 1e-3))))
+        what = f"a sample: the first {rows} rows (all rows if fewer) of every shape"
     flop, t = run(rows)
-    return {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {rows} rows (all rows if fewer) of every shape, cast + GEMM: "
-                      f"{flop / 2e9:.1f} G MAC in {t:.1f} s"}
+    rec = {"value": round(flop / t / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{what}, cast + GEMM: {flop / 2e9:.1f} G MAC in {t:.1f} s",
+           "threads": threads}
+    rec.update(host_description())
+    return rec
 
 
 if __name__ == "__main__":

@@ -53,6 +53,7 @@ _SIGNATURES = {
     "fp8_cast_per_token_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
     "fp8_cast_per_block": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
     "fp8_gemm_describe": ([_i32, _i32, _i32, ctypes.c_char_p, _sz], _i32),
+    "fp8_gemm_schedule": ([_i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32], _i32),
     "fp8_gemm_nt_fmt": ([_vp, _i32, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "fp8_cast_per_token_group_fmt": ([_vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
     "fp8_cast_per_block_fmt": ([_vp, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
@@ -493,6 +494,23 @@ def fp8_gemm_describe(m: int, n: int, k: int) -> str:
     st = lib().fp8_gemm_describe(m, n, k, buf, len(buf))
     _check("fp8_gemm_describe", st)
     return buf.value.decode()
+
+
+def fp8_gemm_schedule(mode, m, n, k, num_groups=0, group_data=None):
+    """Host only: the work unit each workgroup of the GEMM call takes, as an
+    int32 numpy array [workgroups][6] of (taken, group, first row, rows,
+    column tile, split) in launch order.  group_data is a host int32 array
+    (contiguous: m_indices; masked: masked_m)."""
+    import numpy as np
+    gd = None if group_data is None else np.ascontiguousarray(group_data, dtype=np.int32)
+    gp = None if gd is None else gd.ctypes.data_as(ctypes.c_void_p)
+    count = lib().fp8_gemm_schedule(mode, m, n, k, num_groups, gp, None, 0)
+    _check("fp8_gemm_schedule", min(count, 0))
+    units = np.zeros((max(count, 1), 6), np.int32)
+    got = lib().fp8_gemm_schedule(mode, m, n, k, num_groups, gp, units.ctypes.data_as(ctypes.c_void_p), count)
+    _check("fp8_gemm_schedule", min(got, 0))
+    assert got == count
+    return units[:count]
 
 
 def fp8_set_num_cus(num_cus: int) -> int:

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <vector>
 
 #include "fp8gemm.h"
 #include "cast_kernel.hpp"
@@ -106,6 +107,107 @@ int fp8_gemm_describe(int m, int n, int k, char* buf, size_t len) {
   std::snprintf(buf, len, "tile=%dx%d waves=%d stages=%d ku=%d splits=%d grid=%lld", ks.bm, ks.bn, ks.waves,
                 ks.stages, ks.ku, c.splits, (long long)(int64_t(c.tiles_m) * c.tiles_n * c.splits));
   return FP8G_OK;
+}
+
+int fp8_gemm_schedule(int mode, int m, int n, int k, int num_groups, const int32_t* group_data, int32_t* units,
+                      int capacity) {
+  using namespace fp8g;
+  if (m < 0 || num_groups < 0 || capacity < 0 || (capacity > 0 && !units)) return FP8G_EINVAL;
+  if (mode != FP8G_JIT_DENSE && mode != FP8G_JIT_CONTIGUOUS && mode != FP8G_JIT_MASKED) return FP8G_EINVAL;
+  if (const int st = check_gemm_shape(n, k)) return st;
+  if (mode == FP8G_JIT_CONTIGUOUS && m % 128 != 0) return FP8G_EUNSUPPORTED;
+  if (m == 0 || n == 0 || (mode != FP8G_JIT_DENSE && num_groups == 0)) return 0;
+  if (mode != FP8G_JIT_DENSE && !group_data) return FP8G_EINVAL;
+
+  // The launch parameters the entry point would use (the dense one with a
+  // large enough workspace), then every workgroup of every launch that
+  // launch_units makes, decoded as the kernel decodes it.
+  GemmParams p{};
+  int bm = 0;
+  int64_t grid = 0;
+  if (mode == FP8G_JIT_DENSE) {
+    const DenseConfig c = dense_config(m, n, k, true);
+    bm = kShapes[c.kind].bm;
+    p.tiles_m = c.tiles_m; p.tiles_n = c.tiles_n; p.splits = c.splits;
+    grid = int64_t(c.tiles_m) * c.tiles_n * c.splits;
+  } else if (mode == FP8G_JIT_CONTIGUOUS) {
+    bm = kContiguousShape.bm;
+    p.tiles_m = m / 128; p.tiles_n = int(cdiv(n, kContiguousShape.bn)); p.splits = 1;
+    grid = int64_t(p.tiles_m) * p.tiles_n;
+  } else {
+    bm = kMaskedShape.bm;
+    p.tiles_m = int(cdiv(m, bm)); p.tiles_n = int(cdiv(n, kMaskedShape.bn)); p.splits = 1;
+    grid = int64_t(p.tiles_m) * p.tiles_n * num_groups;
+  }
+  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
+
+  // contiguous: the wave-wide scan, lane by lane (the kernel's steps, the
+  // shuffles replaced by loops over the 64 lanes)
+  const int nblk = m / 128;
+  ContigScan cs[kWave] = {};
+  int contig_tiles = 0;
+  if (mode == FP8G_JIT_CONTIGUOUS) {
+    int run_max = -1;
+    for (int lane = 0; lane < kWave; ++lane) {
+      contig_chunk(lane, nblk, cs[lane].lo, cs[lane].hi);
+      cs[lane].in_rs = lane == 0 ? -1 : run_max;  // max over lanes < this one
+      run_max = std::max(run_max, contig_last_run_start(group_data, cs[lane].lo, cs[lane].hi));
+    }
+    for (int lane = 0; lane < kWave; ++lane) {
+      cs[lane].count = contig_count(group_data, cs[lane].lo, cs[lane].hi, cs[lane].in_rs);
+      cs[lane].base = contig_tiles;
+      contig_tiles += cs[lane].count;
+    }
+  }
+  // masked: the live units of every group, numbered group by group
+  std::vector<int> first_unit;
+  int masked_total = 0;
+  if (mode == FP8G_JIT_MASKED) {
+    for (int g = 0; g < num_groups; ++g) {
+      first_unit.push_back(masked_total);
+      masked_total += masked_live_tiles(group_data[g], m, bm) * p.tiles_n;
+    }
+  }
+
+  int64_t written = 0;
+  auto record = [&](int taken, int group, int row0, int rows, int n_tile, int split) {
+    if (written < capacity) {
+      int32_t* r = units + 6 * written;
+      r[0] = taken; r[1] = group; r[2] = row0; r[3] = rows; r[4] = n_tile; r[5] = split;
+    }
+    ++written;
+  };
+  launch_units(p, grid, [&](int64_t g) {
+    for (int64_t b = 0; b < g; ++b) {
+      const int bid = int(b) + p.unit_offset;
+      if (mode == FP8G_JIT_DENSE) {
+        int mt, nt, sp;
+        dense_tile(xcd_logical(bid, p.units), p.tiles_m, p.tiles_n, p.splits, mt, nt, sp);
+        record(1, 0, mt * bm, std::min(bm, m - mt * bm), nt, sp);
+      } else if (mode == FP8G_JIT_CONTIGUOUS) {
+        if (bid >= contig_tiles * p.tiles_n) { record(0, -1, 0, 0, 0, 0); continue; }
+        int t, nt, sp;
+        dense_tile(xcd_logical(bid, contig_tiles * p.tiles_n), contig_tiles, p.tiles_n, 1, t, nt, sp);
+        int block = -1;
+        for (int lane = 0; lane < kWave && block < 0; ++lane)
+          block = contig_find(group_data, cs[lane].lo, cs[lane].hi, cs[lane].in_rs, cs[lane].base, cs[lane].count, t);
+        if (block < 0) { record(0, -2, 0, 0, 0, 0); continue; }  // no lane holds the tile: a scheduler bug
+        record(1, block_group(group_data, block), 128 * block, 128 * contig_tile_blocks(group_data, nblk, block), nt,
+               0);
+      } else {
+        const int L = xcd_logical(bid, masked_total);
+        if (L < 0) { record(0, -1, 0, 0, 0, 0); continue; }
+        const int g = int(std::upper_bound(first_unit.begin(), first_unit.end(), L) - first_unit.begin()) - 1;
+        const int mt = masked_live_tiles(group_data[g], m, bm);
+        const int r = L - first_unit[g];
+        const int rows = std::min(std::max(group_data[g], 0), m);
+        const int row0 = (r % mt) * bm;
+        record(1, g, row0, std::min(bm, rows - row0), r / mt, 0);
+      }
+    }
+    return 0;
+  });
+  return int(written);
 }
 
 int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,

@@ -188,7 +188,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 // negative index belong to no tile.  The host cannot know the tile count,
 // so every wave derives it from the (L2-resident) index array by a
 // wave-wide scan: lane j walks blocks [lo, hi), the j-th chunk of the
-// blocks.
+// blocks.  The per-lane steps below are plain functions (the host's
+// scheduler check runs them too); the wave combines them with shuffles.
 struct ContigScan {
   int tiles;  // tiles in total (the same in every lane)
   int lo, hi;
@@ -197,21 +198,73 @@ struct ContigScan {
   int count;  // tiles that start in this lane's chunk
 };
 
-__device__ __forceinline__ int block_group(const int32_t* idx, int b) { return idx[int64_t(b) * 128]; }
+__host__ __device__ inline int block_group(const int32_t* idx, int b) { return idx[int64_t(b) * 128]; }
 
-__device__ __forceinline__ ContigScan contiguous_scan(const int32_t* idx, int nblk) {
-  const int lane = threadIdx.x & (kWave - 1);
+// Lane `lane`'s chunk [lo, hi) of the nblk blocks.
+__host__ __device__ inline void contig_chunk(int lane, int nblk, int& lo, int& hi) {
   const int chunk = (nblk + kWave - 1) / kWave;
-  ContigScan s;
-  s.lo = min(lane * chunk, nblk);
-  s.hi = min(s.lo + chunk, nblk);
-  int last_rs = -1, prev = s.lo > 0 ? block_group(idx, s.lo - 1) : 0;
-  for (int b = s.lo; b < s.hi; ++b) {
+  lo = lane * chunk < nblk ? lane * chunk : nblk;
+  hi = lo + chunk < nblk ? lo + chunk : nblk;
+}
+
+// First block of the last run that starts in [lo, hi), or -1.
+__host__ __device__ inline int contig_last_run_start(const int32_t* idx, int lo, int hi) {
+  int last_rs = -1, prev = lo > 0 ? block_group(idx, lo - 1) : 0;
+  for (int b = lo; b < hi; ++b) {
     const int e = block_group(idx, b);
     if (b == 0 || e != prev) last_rs = b;
     prev = e;
   }
-  int v = last_rs;  // inclusive max-scan over lanes
+  return last_rs;
+}
+
+// Walks [lo, hi) with in_rs the run start in effect before lo: calls
+// f(b) for every block b that starts a tile (an even offset from its run's
+// first block, non-negative index) until f returns true; returns the number
+// of tile starts visited.
+template <typename F>
+__host__ __device__ inline int contig_walk(const int32_t* idx, int lo, int hi, int in_rs, F&& f) {
+  int cur = in_rs, cnt = 0, prev = lo > 0 ? block_group(idx, lo - 1) : 0;
+  for (int b = lo; b < hi; ++b) {
+    const int e = block_group(idx, b);
+    if (b == 0 || e != prev) cur = b;
+    prev = e;
+    if (e >= 0 && ((b - cur) & 1) == 0) {
+      if (f(b)) break;
+      ++cnt;
+    }
+  }
+  return cnt;
+}
+
+// Tiles that start in [lo, hi).
+__host__ __device__ inline int contig_count(const int32_t* idx, int lo, int hi, int in_rs) {
+  return contig_walk(idx, lo, hi, in_rs, [](int) { return false; });
+}
+
+// First block of tile t if it starts in this lane's chunk (tiles base ..
+// base + count - 1 do), else -1.
+__host__ __device__ inline int contig_find(const int32_t* idx, int lo, int hi, int in_rs, int base, int count, int t) {
+  if (t < base || t >= base + count) return -1;
+  int found = -1, k = base;
+  contig_walk(idx, lo, hi, in_rs, [&](int b) {
+    if (k == t) { found = b; return true; }
+    ++k;
+    return false;
+  });
+  return found;
+}
+
+// Blocks (1 or 2) of the tile that starts at `block`.
+__host__ __device__ inline int contig_tile_blocks(const int32_t* idx, int nblk, int block) {
+  return (block + 1 < nblk && block_group(idx, block + 1) == block_group(idx, block)) ? 2 : 1;
+}
+
+__device__ __forceinline__ ContigScan contiguous_scan(const int32_t* idx, int nblk) {
+  const int lane = threadIdx.x & (kWave - 1);
+  ContigScan s;
+  contig_chunk(lane, nblk, s.lo, s.hi);
+  int v = contig_last_run_start(idx, s.lo, s.hi);  // inclusive max-scan over lanes
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) {
     const int t = __shfl_up(v, d, kWave);
@@ -219,14 +272,7 @@ __device__ __forceinline__ ContigScan contiguous_scan(const int32_t* idx, int nb
   }
   const int excl = __shfl_up(v, 1, kWave);
   s.in_rs = lane == 0 ? -1 : excl;
-  int cur = s.in_rs, cnt = 0;
-  prev = s.lo > 0 ? block_group(idx, s.lo - 1) : 0;
-  for (int b = s.lo; b < s.hi; ++b) {
-    const int e = block_group(idx, b);
-    if (b == 0 || e != prev) cur = b;
-    prev = e;
-    if (e >= 0 && ((b - cur) & 1) == 0) ++cnt;
-  }
+  const int cnt = contig_count(idx, s.lo, s.hi, s.in_rs);
   s.count = cnt;
   int incl = cnt;  // inclusive sum-scan over lanes
 #pragma unroll
@@ -242,24 +288,39 @@ __device__ __forceinline__ ContigScan contiguous_scan(const int32_t* idx, int nb
 // First block, block count (1 or 2) and group of tile t (0 <= t < tiles).
 __device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int32_t* idx, int nblk, int t,
                                                   int& block, int& nblocks, int& group) {
-  int found = -1;
-  if (t >= s.base && t < s.base + s.count) {
-    int cur = s.in_rs, k = s.base, prev = s.lo > 0 ? block_group(idx, s.lo - 1) : 0;
-    for (int b = s.lo; b < s.hi; ++b) {
-      const int e = block_group(idx, b);
-      if (b == 0 || e != prev) cur = b;
-      prev = e;
-      if (e >= 0 && ((b - cur) & 1) == 0) {
-        if (k == t) { found = b; break; }
-        ++k;
-      }
-    }
-  }
+  const int found = contig_find(idx, s.lo, s.hi, s.in_rs, s.base, s.count, t);
   const unsigned long long who = __ballot(found >= 0);
   block = uniform(__shfl(found, __ffsll(who) - 1, kWave));
   group = uniform(block_group(idx, block));
-  nblocks = (block + 1 < nblk && block_group(idx, block + 1) == group) ? 2 : 1;
-  nblocks = uniform(nblocks);
+  nblocks = uniform(contig_tile_blocks(idx, nblk, block));
+}
+
+// Logical unit of workgroup `bid` when `total` units are dealt to the XCDs:
+// workgroups reach the 8 XCDs round-robin (bid % 8) and each XCD has its
+// own L2, so XCD x takes the x-th contiguous share of the logical order
+// (shares differ by at most one unit).  -1 when this workgroup's slot is
+// past its XCD's share.  A bijection from the workgroups with a unit onto
+// [0, total), so correctness does not depend on the dispatch order.
+__host__ __device__ inline int xcd_logical(int bid, int total) {
+  const int xcd = bid % kXcds, slot = bid / kXcds;
+  const int per = total / kXcds, extra = total % kXcds;
+  if (slot >= per + (xcd < extra ? 1 : 0)) return -1;
+  return (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
+}
+
+// Dense (and contiguous) tile of logical unit L: the split fastest, then
+// bands of kGroupM M-tiles by all N-tiles, M fastest within a band, so the
+// tiles an XCD runs at once share a few A and B K-slices.
+__host__ __device__ inline void dense_tile(int L, int tiles_m, int tiles_n, int splits, int& m_tile, int& n_tile,
+                                           int& split) {
+  split = L % splits;
+  L /= splits;
+  const int band = kGroupM * tiles_n;
+  const int first_m = (L / band) * kGroupM;
+  const int rows_in_band = tiles_m - first_m < kGroupM ? tiles_m - first_m : kGroupM;
+  const int in_band = L % band;
+  m_tile = first_m + in_band % rows_in_band;
+  n_tile = in_band / rows_in_band;
 }
 
 // Work units of the masked layout.  Group g has ceil(rows_g / BM) live row
@@ -272,11 +333,16 @@ __device__ __forceinline__ void contiguous_locate(const ContigScan& s, const int
 // (not by all eight), and every XCD gets the same number of live units.
 // Every wave derives the numbering from the (L2-resident) counts.  Returns
 // false for a workgroup past the live units of its XCD.
+__host__ __device__ inline int masked_live_tiles(int count, int max_m, int bm) {
+  const int rows = count < 0 ? 0 : (count > max_m ? max_m : count);
+  return (rows + bm - 1) / bm;
+}
+
 template <int BM>
 __device__ __forceinline__ bool masked_unit(const int32_t* masked_m, int groups, int max_m, int tiles_n, int bid,
                                             int& group, int& m_tile, int& n_tile) {
   const int lane = threadIdx.x & (kWave - 1);
-  auto live_tiles = [&](int g) { return g < groups ? (min(max(masked_m[g], 0), max_m) + BM - 1) / BM : 0; };
+  auto live_tiles = [&](int g) { return g < groups ? masked_live_tiles(masked_m[g], max_m, BM) : 0; };
   auto inclusive_sum = [&](int v) {
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
@@ -288,10 +354,8 @@ __device__ __forceinline__ bool masked_unit(const int32_t* masked_m, int groups,
   int total = 0;  // live units (< the grid size, so no overflow)
   for (int g0 = 0; g0 < groups; g0 += kWave)
     total += uniform(__shfl(inclusive_sum(live_tiles(g0 + lane) * tiles_n), kWave - 1, kWave));
-  const int xcd = bid % kXcds, slot = bid / kXcds;
-  const int per = total / kXcds, extra = total % kXcds;
-  if (slot >= per + (xcd < extra ? 1 : 0)) return false;
-  const int L = (xcd < extra ? xcd * (per + 1) : extra * (per + 1) + (xcd - extra) * per) + slot;
+  const int L = xcd_logical(bid, total);
+  if (L < 0) return false;
   int base = 0;
   for (int g0 = 0; g0 < groups; g0 += kWave) {
     const int mt = live_tiles(g0 + lane);
@@ -333,7 +397,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 sub-tiles");
   static_assert(WN <= 128 && 128 % WN == 0, "a wave's n range stays inside one RHS scale block");
   static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0 && BM <= 256, "whole 1 KB copies; scales in one copy");
-  static_assert(STAGES >= 2 && STAGES <= 8 && KU >= 1 && KU <= 4 && KU % WK == 0, "ring depth");
+  // STAGES == 1 is the single-buffer debug form: each stage's copies are
+  // issued only after every wave has finished reading the previous one, so
+  // loads never overlap the products ("DeepGEMM: FP8 GEMM kernel
+  // optimisation practice on Hopper Tensor Cores", section 6.2: fall back
+  // to one buffer to tell a pipeline race from an arithmetic error).
+  static_assert(STAGES >= 1 && STAGES <= 8 && KU >= 1 && KU <= 4 && KU % WK == 0, "ring depth");
   // LDS: [STAGES * KU][BM][128 B] LHS tiles, then [STAGES * KU][BN][128 B]
   // RHS tiles, then [STAGES * KU][BM] LHS scales (one group per slot, KU
   // slots per stage), then the tile's RHS scale rows.
@@ -385,22 +454,9 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     if (bid >= tiles_m * p.tiles_n) return;
   }
   if constexpr (MODE == kDense || MODE == kContiguous) {
-    // Workgroups are dispatched to the 8 XCDs round-robin and each XCD has
-    // its own L2: give XCD x a contiguous range of logical tiles, walked in
-    // groups of kGroupM M-tiles (M fastest), so the tiles an XCD runs at
-    // once share a few A and B K-slices.  (A bijection, so correctness does
-    // not depend on the dispatch order.)
-    const int total = MODE == kContiguous ? tiles_m * p.tiles_n : p.units;
-    const int xcd = bid % kXcds, slot = bid / kXcds;
-    const int per = total / kXcds, extra = total % kXcds;
-    int L = xcd < extra ? xcd * (per + 1) + slot : extra * (per + 1) + (xcd - extra) * per + slot;
-    if constexpr (SPLIT) { split = L % p.splits; L /= p.splits; }
-    const int band = kGroupM * p.tiles_n;
-    const int first_m = (L / band) * kGroupM;
-    const int rows_in_band = min(tiles_m - first_m, kGroupM);
-    const int in_band = L % band;
-    m_tile = first_m + in_band % rows_in_band;
-    n_tile = in_band / rows_in_band;
+    // (every workgroup below the unit count has a unit: bid < total)
+    const int L = xcd_logical(bid, MODE == kContiguous ? tiles_m * p.tiles_n : p.units);
+    dense_tile(L, tiles_m, p.tiles_n, SPLIT ? p.splits : 1, m_tile, n_tile, split);
   } else {
     // (p.units counts every possible unit: groups x tiles_m x tiles_n)
     if (!masked_unit<BM>(p.masked_m, p.units / (p.tiles_m * p.tiles_n), p.m, p.tiles_n, bid, group,
@@ -525,7 +581,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   f.s = reinterpret_cast<const float*>(smem + S_REGION + wk * S_BYTES) + wrow_m + lr;
 
   // (the scale-row copies above are older)
-  static_for<0, STAGES - 1>([&](auto ic) __attribute__((always_inline)) {
+  static_for<0, (STAGES > 1 ? STAGES - 1 : 1)>([&](auto ic) __attribute__((always_inline)) {
     constexpr int I = decltype(ic)::value;
     if (I < niter) issue(Int<I>{}, I);
   });
@@ -535,7 +591,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     wait_stage<STAGES, STAGE_COPIES>(min(STAGES - 2, niter - 1 - it));
     wait_lgkmcnt0();
     block_barrier();
-    if (it + STAGES - 1 < niter) issue(Int<(stage + STAGES - 1) % STAGES>{}, it + STAGES - 1);
+    if constexpr (STAGES > 1)
+      if (it + STAGES - 1 < niter) issue(Int<(stage + STAGES - 1) % STAGES>{}, it + STAGES - 1);
     if (wave_live)
       static_for<0, KU / WK>([&](auto uc) __attribute__((always_inline)) {
         constexpr int slot = stage * KU + decltype(uc)::value * WK;  // + wk, folded into f
@@ -543,6 +600,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
         if (KU == 1 || gl < ngroups)
           group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES, FMT>(acc, f, sb_row[gl]);
       });
+    if constexpr (STAGES == 1) {
+      // every wave's reads of the only slot are done before it is refilled
+      wait_lgkmcnt0();
+      block_barrier();
+      if (it + 1 < niter) issue(Int<0>{}, it + 1);
+    }
   };
   // Kept rolled: with k a compile-time constant the compiler would unroll
   // the whole K loop, run out of registers and spill, and spill traffic

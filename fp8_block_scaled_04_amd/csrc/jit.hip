@@ -152,6 +152,7 @@ struct Loaded {
   hipFunction_t fn = nullptr;
 };
 std::unordered_map<std::string, Loaded> g_loaded;  // "<device>|<key>" -> kernel
+std::unordered_set<std::string> g_refused;                  // "<device>|<key>" of refused builds
 
 // ---- configurations ------------------------------------------------------
 bool valid_config(const fp8_gemm_config& c, int mode) {
@@ -162,7 +163,7 @@ bool valid_config(const fp8_gemm_config& c, int mode) {
   const int wm = c.block_m / c.waves_m, wn = c.block_n / c.waves_n;
   if (wm % 16 || wn % 16 || wn > 128 || 128 % wn) return false;
   if (c.block_m % (8 * nw) || c.block_n % (8 * nw)) return false;
-  if (c.stages < 2 || c.stages > 8 || c.k_per_stage < 1 || c.k_per_stage > 4 || c.k_per_stage % c.waves_k)
+  if (c.stages < 1 || c.stages > 8 || c.k_per_stage < 1 || c.k_per_stage > 4 || c.k_per_stage % c.waves_k)
     return false;
   const int copies = c.k_per_stage * (c.block_m / (8 * nw) + c.block_n / (8 * nw));
   if ((c.stages - 2) * copies >= 64) return false;  // vmcnt range
@@ -362,8 +363,13 @@ long long private_segment_size(const std::vector<char>& code) {
   return worst;
 }
 
+// Name stored in a cache entry for a configuration whose build was refused
+// (it needs scratch memory): later processes skip the doomed compilation.
+const char kRefusedName[] = "!refused: needs scratch memory";
+
 int compile(const std::string& dir, const std::string& arch, const std::string& key, const Program& prog,
-            std::vector<char>* code) {
+            std::vector<char>* code, bool* refused) {
+  *refused = false;
   const auto t0 = std::chrono::steady_clock::now();
   // the embedded headers, once per kernel-source digest
   char sub[48];
@@ -412,6 +418,7 @@ int compile(const std::string& dir, const std::string& arch, const std::string& 
   // copies that the ring waits count.
   if (private_segment_size(*code) != 0) {
     g_stat[kFailed]++;
+    *refused = true;
     if (jit_debug() || log_enabled())
       std::fprintf(stderr, "[fp8gemm jit] %s needs scratch memory (register spills): refused\n",
                    prog.expr.c_str());
@@ -440,6 +447,10 @@ int get_kernel(const Program& prog, hipFunction_t* fn) {
   {
     std::unique_lock<std::mutex> lock(g_mu);
     g_built.wait(lock, [&] { return g_building.count(mem_key) == 0; });
+    if (g_refused.count(mem_key)) {
+      g_stat[kMemHit]++;
+      return FP8G_EUNSUPPORTED;
+    }
     if (device >= 0) {
       auto it = g_loaded.find(mem_key);
       if (it != g_loaded.end()) {
@@ -452,17 +463,32 @@ int get_kernel(const Program& prog, hipFunction_t* fn) {
     dir = cache_dir_locked();
   }
   Loaded l;
+  bool refused_here = false;
   const int st = [&] {
     const std::string path = cache_file(dir, key);
     std::string name;
     std::vector<char> code;
-    bool rejected = false;
-    if (read_cached(path, key, &name, &code, &rejected) && name == prog.symbol) {
+    bool rejected = false, refused = false;
+    const bool cached = read_cached(path, key, &name, &code, &rejected);
+    if (cached && name == kRefusedName) {
+      g_stat[kDiskHit]++;
+      if (jit_debug()) std::fprintf(stderr, "[fp8gemm jit] %s refused (recorded in %s)\n", prog.expr.c_str(),
+                                    path.c_str());
+      refused_here = true;
+      return int(FP8G_EUNSUPPORTED);
+    }
+    if (cached && name == prog.symbol) {
       g_stat[kDiskHit]++;
       if (jit_debug()) std::fprintf(stderr, "[fp8gemm jit] %s from %s\n", prog.expr.c_str(), path.c_str());
     } else {
       if (rejected) g_stat[kRejected]++;
-      if (const int c = compile(dir, arch, key, prog, &code)) return c;
+      if (const int c = compile(dir, arch, key, prog, &code, &refused)) {
+        if (refused) {  // remembered on disk: later processes do not rebuild it
+          write_cached(dir, path, key, kRefusedName, std::vector<char>());
+          refused_here = true;
+        }
+        return c;
+      }
       name = prog.symbol;
       write_cached(dir, path, key, name, code);
     }
@@ -477,6 +503,7 @@ int get_kernel(const Program& prog, hipFunction_t* fn) {
   {
     std::lock_guard<std::mutex> lock(g_mu);
     if (st == FP8G_OK && l.fn) g_loaded[mem_key] = l;  // kept until the process ends
+    if (refused_here) g_refused.insert(mem_key);
     g_building.erase(mem_key);
   }
   g_built.notify_all();
@@ -499,6 +526,15 @@ int launch(const Program& prog, const GemmParams& p, int64_t grid, void* stream)
     }
     return launched("jit gemm");
   });
+}
+
+// FP8G_PIPELINE_DEPTH=d (debugging): every runtime-specialised kernel is
+// built with a ring of d stages, d = 1 being the single-buffer form in which
+// no copy overlaps the products (a pipeline race then disappears, an
+// arithmetic error does not).
+void apply_debug_depth(fp8_gemm_config& c) {
+  const int d = env_int("FP8G_PIPELINE_DEPTH", 0);
+  if (d > 0) c.stages = d;
 }
 
 int format_code(int lhs_format, int rhs_format, int* fmt) {
@@ -554,6 +590,7 @@ int fp8_jit_warmup(int mode, int n, int k, int lhs_format, int rhs_format, const
   fp8_gemm_config c{};
   if (config) c = *config;
   else if (const int st = fp8_jit_default_config(mode, 1, n, k, &c)) return st;
+  apply_debug_depth(c);
   if (!valid_config(c, mode)) return FP8G_EUNSUPPORTED;
   hipFunction_t fn = nullptr;
   return get_kernel(program_for(c, mode, fmt, n, k), &fn);
@@ -580,6 +617,7 @@ int fp8_jit_gemm_nt(const uint8_t* lhs, int lhs_format, const float* lhs_scales,
   fp8_gemm_config c{};
   if (config) c = *config;
   else fp8_jit_default_config(FP8G_JIT_DENSE, m, n, k, &c);
+  apply_debug_depth(c);
   if (!valid_config(c, FP8G_JIT_DENSE)) return FP8G_EUNSUPPORTED;
   DenseConfig d = dense_tiling(c, m, n, k);
   if (d.splits > 1 && (!workspace || workspace_bytes < dense_workspace(d, m, n))) {
@@ -616,6 +654,7 @@ int fp8_jit_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales,
   if (const int st = check_ld(lhs_scales_ld, m_total)) return st;
   fp8_gemm_config c = from_shape(kContiguousShape, 1);
   if (config) c = *config;
+  apply_debug_depth(c);
   if (!valid_config(c, FP8G_JIT_CONTIGUOUS)) return FP8G_EUNSUPPORTED;
   GemmParams p{};
   p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
@@ -640,6 +679,7 @@ int fp8_jit_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int
   if (const int st = check_ld(lhs_scales_ld, max_m)) return st;
   fp8_gemm_config c = from_shape(kMaskedShape, 1);
   if (config) c = *config;
+  apply_debug_depth(c);
   if (!valid_config(c, FP8G_JIT_MASKED)) return FP8G_EUNSUPPORTED;
   GemmParams p{};
   p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;

@@ -95,6 +95,29 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
  * FP8G_EUNSUPPORTED for n, k fp8_gemm_nt rejects. */
 int fp8_gemm_describe(int m, int n, int k, char* buf, size_t len);
 
+/* Host only, launches nothing: the tile scheduler's decision for every
+ * workgroup of a GEMM call, for checking the scheduler without a device.
+ * "DeepSeek open-source week, day 3: DeepGEMM" lets the grouped kinds skip
+ * what has no work (the contiguous kind's per-row group index, the masked
+ * kind's device-side counts); this reports which work unit each workgroup
+ * takes, decoded by the same functions the kernels run, across the
+ * consecutive launches a CU limit (fp8_set_num_cus) makes.
+ *   mode        FP8G_JIT_DENSE (the configuration fp8_gemm_nt picks with a
+ *               large enough workspace), FP8G_JIT_CONTIGUOUS or
+ *               FP8G_JIT_MASKED (the ahead-of-time grouped kernels)
+ *   m           dense: m; contiguous: m_total; masked: max_m
+ *   group_data  HOST int32 array: contiguous m_indices [m]; masked
+ *               masked_m [num_groups]; dense: unused (may be NULL)
+ *   units       HOST int32 [capacity][6], one record per workgroup in launch
+ *               order: {taken (1 = has a unit, 0 = exits), group, first row,
+ *               rows, column tile, split}; records past capacity are not
+ *               written
+ * Returns the number of workgroups of the call (>= 0), or a negative status
+ * (FP8G_EINVAL for bad arguments, FP8G_EUNSUPPORTED for shapes the GEMM
+ * entry points reject). */
+int fp8_gemm_schedule(int mode, int m, int n, int k, int num_groups, const int32_t* group_data,
+                      int32_t* units, int capacity);
+
 /* fp8_gemm_nt with each operand's format given: lhs_format / rhs_format are
  * FP8G_E4M3 or FP8G_E5M2, in any combination (FP8G_EINVAL otherwise).  The
  * arithmetic is the same; only the decoding of the codes changes. */

@@ -67,7 +67,7 @@ def test_default_config_is_the_ahead_of_time_choice(lib):
     cfg(waves_m=3, waves_n=1),                     # 3 waves
     cfg(block_m=320),                              # > 256 rows
     cfg(block_n=96, waves_n=2),                    # a wave's 48 columns do not divide 128
-    cfg(stages=9), cfg(stages=1), cfg(k_per_stage=5),
+    cfg(stages=9), cfg(stages=0), cfg(k_per_stage=5),
     cfg(k_per_stage=3, waves_k=2, waves_m=1),      # k_per_stage not a multiple of waves_k
     cfg(block_m=256, block_n=256, waves_m=4, waves_n=2, stages=3),   # LDS over 160 KB
     cfg(block_m=256, block_n=256, waves_m=2, waves_n=2, stages=2),   # 128 x 128 per wave: registers
@@ -214,3 +214,57 @@ def test_concurrent_warmups_compile_each_kernel_once(cache):
     assert not errors
     assert d["compiles"] == 2 and d["disk_hits"] == 4 and d["failed_compiles"] == 0
     assert len(code_files(cache)) == 2
+
+
+def test_single_stage_debug_form_builds(cache, monkeypatch):
+    """stages = 1 is the single-buffer form (each stage's copies issued only
+    after every wave has read the previous one; "DeepGEMM: FP8 GEMM kernel
+    optimisation practice on Hopper Tensor Cores", section 6.2), and
+    FP8G_PIPELINE_DEPTH=1 turns every runtime-specialised kernel into it."""
+    c = cfg(stages=1)
+    assert binding.fp8_jit_config_supported(D, c)
+    binding.fp8_jit_warmup(D, 1024, 1024, config=c)
+    monkeypatch.setenv("FP8G_PIPELINE_DEPTH", "1")
+    binding.fp8_jit_warmup(D, 2112, 7168)                 # the default configuration, one stage
+    blobs = b"".join((cache / f).read_bytes() for f in code_files(cache))
+    assert b"_ZN4fp8g11gemm_kernelILi128ELi128ELi2ELi2ELi1ELi0ELb0E" in blobs
+    d = binding.fp8_jit_default_config(D, 1, 2112, 7168)
+    assert f"_ZN4fp8g11gemm_kernelILi{d.block_m}ELi{d.block_n}ELi{d.waves_m}ELi{d.waves_n}ELi1E".encode() in blobs
+
+
+def test_refused_build_is_remembered_across_processes(cache):
+    """A configuration whose build needs scratch memory (here the 256 x 256
+    tile with n and k compiled in) is refused; the refusal is recorded in the
+    cache, so another process refuses it without compiling again."""
+    import ast
+    import subprocess
+    import sys
+    c = cfg(block_m=256, block_n=256, waves_m=4, waves_n=2, stages=2, specialize=1)
+    before = binding.fp8_jit_stats()
+    with pytest.raises(binding.Fp8GemmError) as e:
+        binding.fp8_jit_warmup(D, 4096, 7168, config=c)
+    assert e.value.status == binding.FP8G_EUNSUPPORTED
+    d = delta(before, binding.fp8_jit_stats())
+    assert d["failed_compiles"] == 1 and d["compiles"] == 0
+    assert len(code_files(cache)) == 1                     # the refusal record
+    before = binding.fp8_jit_stats()                        # again in this process: from memory
+    with pytest.raises(binding.Fp8GemmError):
+        binding.fp8_jit_warmup(D, 4096, 7168, config=c)
+    d = delta(before, binding.fp8_jit_stats())
+    assert d["failed_compiles"] == 0 and d["memory_hits"] == 1
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from fp8_block_scaled_04_amd import binding\n"
+        "binding.fp8_jit_set_cache_dir(%r)\n"
+        "try:\n"
+        "    binding.fp8_jit_warmup(0, 4096, 7168, config=%r)\n"
+        "    print('built')\n"
+        "except binding.Fp8GemmError as e:\n"
+        "    print('refused', e.status)\n"
+        "print(binding.fp8_jit_stats())\n" % (root, str(cache), c))
+    out = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=300,
+                         env={**os.environ, "HIP_VISIBLE_DEVICES": "-1"}).stdout.splitlines()
+    assert out[0] == f"refused {binding.FP8G_EUNSUPPORTED}", out
+    stats = ast.literal_eval(out[1])                         # the dict the child printed
+    assert stats["failed_compiles"] == 0 and stats["compiles"] == 0 and stats["disk_hits"] == 1

@@ -106,14 +106,35 @@ struct FragPtrs {
 // one fragment ahead.  Each MFMA is issued before the promotion of the
 // previous product, so the promotion FMAs run while the next MFMA occupies
 // the matrix core.
-template <int TM, int TN, int A_SLOT, int B_SLOT, int S_SLOT, int FMT = 0>
-__device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs& f, float sbv) {
+// ROW_GUARD (masked layout): only the wave's first live_tm 16-row sub-tiles
+// of tokens hold rows below the group's count; the products of the others
+// are skipped (their outputs are never stored), so no MFMA or promotion is
+// spent on rows past the count.  Each 16-row sub-tile's products are then
+// promoted within its own (wave-uniform) branch.
+template <int TM, int TN, int A_SLOT, int B_SLOT, int S_SLOT, int FMT = 0, bool ROW_GUARD = false>
+__device__ __forceinline__ void group_product(v4f (&acc)[TN][TM], const FragPtrs& f, float sbv, int live_tm = TM) {
   constexpr int FB = (FMT >> 1) & 1, FA = FMT & 1;  // src0 = RHS fragment, src1 = LHS fragment
   constexpr int FRAG = 16 * kRowBytes;
   auto afrag = [&](int j) { return lds_frag(f.a0 + A_SLOT + j * FRAG, f.a1 + A_SLOT + j * FRAG); };
   auto bfrag = [&](int i) { return lds_frag(f.b0 + B_SLOT + i * FRAG, f.b1 + B_SLOT + i * FRAG); };
   auto ascale = [&](int j) { return f.s[S_SLOT / 4 + 16 * j] * sbv; };
-  if constexpr (TN <= TM) {
+  if constexpr (ROW_GUARD) {
+    v8i bf[TN];
+#pragma unroll
+    for (int i = 0; i < TN; ++i) bf[i] = bfrag(i);
+#pragma unroll
+    for (int j = 0; j < TM; ++j) {
+      if (j < live_tm) {
+        const v8i a = afrag(j);
+        const float sc = ascale(j);
+        v4f pr[TN];
+#pragma unroll
+        for (int i = 0; i < TN; ++i) pr[i] = mfma16x16x128<FB, FA>(bf[i], a);
+#pragma unroll
+        for (int i = 0; i < TN; ++i) promote(acc[i][j], pr[i], sc);
+      }
+    }
+  } else if constexpr (TN <= TM) {
     v8i bf[TN];
 #pragma unroll
     for (int i = 0; i < TN; ++i) bf[i] = bfrag(i);
@@ -419,9 +440,12 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   // After the K loop the ring holds the BF16 output tile on its way out
   // (rows padded by 8 elements so that neither the fragment-ordered writes
   // nor the row-ordered reads pile onto a few banks).
+  // A split's FP32 partial tile is staged the same way (rows padded by 4).
   constexpr int OUT_LDT = BN + 8;
   constexpr int OUT_BYTES = BM * OUT_LDT * 2;
-  constexpr int SMEM = RING > OUT_BYTES ? RING : OUT_BYTES;
+  constexpr int PART_BYTES = SPLIT ? BM * (BN + 4) * 4 : 0;
+  constexpr int SMEM = RING > OUT_BYTES ? (RING > PART_BYTES ? RING : PART_BYTES)
+                                        : (OUT_BYTES > PART_BYTES ? OUT_BYTES : PART_BYTES);
   static_assert(SMEM + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS with the output staging");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ float sb_cache[SB_BLOCKS][kMaxGroups];
@@ -567,8 +591,10 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   const float* sb_row = sb_cache[wrow_n / 128];
   // A wave whose tokens are all past the tile's valid rows (masked counts,
   // one-block contiguous tiles) skips the products (its copies still run:
-  // the ring is shared).
+  // the ring is shared); in the masked layout a live wave also skips its
+  // 16-row sub-tiles that lie wholly past the count.
   const bool wave_live = MODE == kDense || m0 + wrow_m < rows;
+  const int live_tm = MODE == kMasked ? uniform(min(TM, max(0, (rows - m0 - wrow_m + 15) / 16))) : TM;
 
   // Fragment pointers of ring slot wk (wave and fragment row offsets are
   // multiples of 16, i.e. whole 2 KB blocks).
@@ -598,7 +624,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
         constexpr int slot = stage * KU + decltype(uc)::value * WK;  // + wk, folded into f
         const int gl = KU * it + decltype(uc)::value * WK + wk;
         if (KU == 1 || gl < ngroups)
-          group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES, FMT>(acc, f, sb_row[gl]);
+          group_product<TM, TN, slot * A_BYTES, slot * B_BYTES, slot * S_BYTES, FMT, MODE == kMasked>(
+              acc, f, sb_row[gl], live_tm);
       });
     if constexpr (STAGES == 1) {
       // every wave's reads of the only slot are done before it is refilled
@@ -652,7 +679,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     // accesses, which go past the per-XCD L2s: retiring the stores before
     // the arrival is counted makes them visible to the last workgroup
     // without any cache-wide write-back or invalidate.
-    static_assert(BM * (BN + 4) * 4 <= RING, "staged partial tile fits in the ring");
+    static_assert(BM * (BN + 4) * 4 <= SMEM, "staged partial tile fits");
     constexpr int LDT = BN + 4;  // padded row stride (floats) of the staged tile
     constexpr int CHUNKS = BM * BN / 4;
     float* stage = reinterpret_cast<float*>(smem);

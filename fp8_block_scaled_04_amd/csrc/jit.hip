@@ -171,12 +171,14 @@ bool valid_config(const fp8_gemm_config& c, int mode) {
   const int ring = slots * (c.block_m * 128 + c.block_n * 128 + c.block_m * 4);
   const int sb_blocks = (c.block_n + 127) / 128;
   const int staging = c.block_m * (c.block_n + 8) * 2;  // the BF16 output tile on its way out
-  if (std::max(ring, staging) + sb_blocks * fp8g::kMaxGroups * 4 > 160 * 1024) return false;  // LDS
+  const int partial = c.splits > 1 ? c.block_m * (c.block_n + 4) * 4 : 0;  // a split's FP32 tile
+  if (std::max(std::max(ring, staging), partial) + sb_blocks * fp8g::kMaxGroups * 4 > 160 * 1024)
+    return false;  // LDS
   const int tm = wm / 16, tn = wn / 16;
   if (tm * tn > 32) return false;  // accumulators stay within 128 VGPRs
   if (c.waves_k > 1 && nw * tn * tm * 64 * 16 > ring) return false;
   if (c.splits < 1 || c.splits > kMaxSplits) return false;
-  if (c.splits > 1 && (mode != FP8G_JIT_DENSE || c.block_m * (c.block_n + 4) * 4 > ring)) return false;
+  if (c.splits > 1 && mode != FP8G_JIT_DENSE) return false;
   if (mode == FP8G_JIT_CONTIGUOUS && c.block_m != 256) return false;
   return mode == FP8G_JIT_DENSE || mode == FP8G_JIT_CONTIGUOUS || mode == FP8G_JIT_MASKED;
 }

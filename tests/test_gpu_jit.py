@@ -196,3 +196,41 @@ def test_cu_limit_slices_give_the_same_bits():
         binding.fp8_set_num_cus(prev)
     assert np.array_equal(got, want)
 
+
+
+@pytest.mark.parametrize("mode", ["dense_split", "dense_large", "contiguous", "masked"])
+def test_single_stage_ring_matches_the_oracle(mode, monkeypatch):
+    """The single-buffer debug form (FP8G_PIPELINE_DEPTH=1: one ring stage,
+    each stage's copies issued only after every wave has read the last one;
+    "DeepGEMM: FP8 GEMM kernel optimisation practice on Hopper Tensor
+    Cores", section 6.2) gives results within the bar for every kind."""
+    require_gpu()
+    monkeypatch.setenv("FP8G_PIPELINE_DEPTH", "1")
+    say(f"jit single-stage ring {mode}")
+    if mode.startswith("dense"):
+        m, n, k = (64, 2112, 7168) if mode == "dense_split" else (512, 520, 1280)
+        qa, sa, qb, sb = dense_case(m, n, k, seed=17)
+        assert_close(run_jit(qa, sa, qb, sb), oracle.gemm_nt(qa, sa, qb, sb), f"{mode} {m}x{n}x{k}")
+    elif mode == "contiguous":
+        sizes, n, k = [256, 128, 384], 264, 1024
+        qa, sa, qb, sb, m_idx = contiguous_case(sizes, n, k, seed=18)
+        out = Guarded((qa.shape[0], n))
+        binding.fp8_jit_grouped_gemm_contiguous(dev(qa), dev(sa_mn_major(sa)), dev(qb), dev(sb), out.view,
+                                                dev(m_idx.astype(np.int32)))
+        ref = np.full((qa.shape[0], n), 0x5A5A, np.uint16)
+        oracle.gemm_contiguous(qa, sa, qb, sb, m_idx, ref)
+        assert_close(out.result(), ref, "contiguous, one stage")
+    else:
+        G, max_m, n, k, counts = 3, 128, 264, 1024, [128, 0, 70]
+        qa, sa, qb, sb = masked_case(G, max_m, n, k, counts, seed=19)
+        out = Guarded((G, max_m, n))
+        sa_dev = np.stack([sa_mn_major(sa[g], ld_of(max_m)) for g in range(G)])
+        binding.fp8_jit_grouped_gemm_masked(dev(qa), dev(sa_dev), dev(qb), dev(sb), out.view,
+                                            dev(np.asarray(counts, np.int32)))
+        got = out.result()
+        ref = np.full((G, max_m, n), 0x5A5A, np.uint16)
+        oracle.gemm_masked(qa, sa, qb, sb, np.asarray(counts, np.int32), ref)
+        for g, c in enumerate(counts):
+            assert np.all(got[g, c:] == 0x5A5A)
+        assert_close(np.concatenate([got[g, :c].ravel() for g, c in enumerate(counts)]),
+                     np.concatenate([ref[g, :c].ravel() for g, c in enumerate(counts)]), "masked, one stage")

@@ -23,7 +23,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = _build.LIB
 HEADER = os.path.join(os.path.dirname(HERE), "include", "fp8gemm.h")
 
-FP8G_OK, FP8G_EINVAL, FP8G_EUNSUPPORTED, FP8G_ELAUNCH = 0, -1, -2, -3
+FP8G_OK, FP8G_EINVAL, FP8G_EUNSUPPORTED, FP8G_ELAUNCH, FP8G_ESCRATCH = 0, -1, -2, -3, -4
 FP8G_F32, FP8G_BF16 = 0, 1
 FP8G_E4M3, FP8G_E5M2 = 0, 1
 FP8G_JIT_DENSE, FP8G_JIT_CONTIGUOUS, FP8G_JIT_MASKED = 0, 1, 2
@@ -52,6 +52,7 @@ _SIGNATURES = {
     "fp8_grouped_gemm_masked": ([_vp, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
     "fp8_cast_per_token_group": ([_vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp], _i32),
     "fp8_cast_per_block": ([_vp, _i32, _i32, _vp, _vp, _vp], _i32),
+    "fp8_gemm_nt_noalloc": ([_vp, _vp, _i64, _vp, _vp, _vp, _i32, _i32, _i32, _vp], _i32),
     "fp8_gemm_describe": ([_i32, _i32, _i32, ctypes.c_char_p, _sz], _i32),
     "fp8_gemm_schedule": ([_i32, _i32, _i32, _i32, _i32, _vp, _vp, _i32], _i32),
     "fp8_gemm_nt_fmt": ([_vp, _i32, _vp, _i64, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp], _i32),
@@ -283,6 +284,20 @@ def fp8_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, workspace=None, stream=No
     st = lib().fp8_gemm_nt(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales), _p(out),
                            m, n, k, _p(workspace), ws_bytes, _stream(stream))
     _check("fp8_gemm_nt", st)
+    return out
+
+
+def fp8_gemm_nt_noalloc(lhs, lhs_scales, rhs, rhs_scales, out, stream=None):
+    """fp8_gemm_nt with no workspace and no allocation: split-K scratch is
+    the library's static per-device array (calls on one device must not
+    overlap)."""
+    lhs, rhs = _codes(lhs, "lhs"), _codes(rhs, "rhs")
+    lhs_scales, rhs_scales = _f32(lhs_scales, "lhs_scales"), _f32(rhs_scales, "rhs_scales")
+    out = _bf16(out, "out")
+    m, n, k = _check_gemm_nt(lhs, lhs_scales, rhs, rhs_scales, out, None)
+    st = lib().fp8_gemm_nt_noalloc(_p(lhs), _p(lhs_scales), lhs_scales.shape[-1], _p(rhs), _p(rhs_scales), _p(out),
+                                   m, n, k, _stream(stream))
+    _check("fp8_gemm_nt_noalloc", st)
     return out
 
 

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstdio>
+#include <mutex>
 #include <vector>
 
 #include "fp8gemm.h"
@@ -66,6 +67,90 @@ void launch_cast_1x128(const void* x, int x_dtype, bool pair, dim3 grid, hipStre
   }
 }
 
+// Host checks shared by the dense entry points (everything the host can
+// check, before any launch); fmt receives the operand-format code.
+int check_dense_args(const uint8_t* lhs, int lhs_format, const float* lhs_scales, int64_t lhs_scales_ld,
+                     const uint8_t* rhs, int rhs_format, const float* rhs_scales, const uint16_t* out, int m, int n,
+                     int k, const void* workspace, int* fmt) {
+  if (m < 0) return FP8G_EINVAL;
+  if ((lhs_format != FP8G_E4M3 && lhs_format != FP8G_E5M2) || (rhs_format != FP8G_E4M3 && rhs_format != FP8G_E5M2))
+    return FP8G_EINVAL;
+  *fmt = (lhs_format == FP8G_E5M2 ? 1 : 0) | (rhs_format == FP8G_E5M2 ? 2 : 0);
+  if (int st = check_gemm_shape(n, k)) return st;
+  if (m == 0 || n == 0) return FP8G_OK;
+  if (!lhs || !lhs_scales || !rhs || !rhs_scales || !out) return FP8G_EINVAL;
+  if (!aligned16(lhs) || !aligned16(lhs_scales) || !aligned16(rhs) || !aligned16(rhs_scales) ||
+      !aligned16(out) || (workspace && !aligned16(workspace)))
+    return FP8G_EINVAL;
+  return check_ld(lhs_scales_ld, m);
+}
+
+// The dense GEMM of checked arguments (m, n > 0): configuration, split-K
+// workspace layout, launches.
+int run_dense_gemm(const uint8_t* lhs, int fmt, const float* lhs_scales, int64_t lhs_scales_ld, const uint8_t* rhs,
+                   const float* rhs_scales, uint16_t* out, int m, int n, int k, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  DenseConfig c = dense_config(m, n, k, true);
+  if (c.splits > 1 && (!workspace || workspace_bytes < dense_workspace(c, m, n)))
+    c = dense_config(m, n, k, false);
+
+  GemmParams p{};
+  p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
+  if (c.splits > 1) {
+    p.tile_counters = static_cast<unsigned long long*>(workspace);
+    p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c));
+    p.epoch = next_epoch();
+  }
+  p.sa_ld = lhs_scales_ld;
+  p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
+  p.tiles_m = c.tiles_m; p.tiles_n = c.tiles_n; p.splits = c.splits; p.groups_per_split = c.gps;
+  const int64_t grid = int64_t(c.tiles_m) * c.tiles_n * c.splits;
+  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
+  auto s = static_cast<hipStream_t>(stream);
+  if (log_enabled())
+    std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
+                 c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
+  return launch_units(p, grid, [&](int64_t g) {
+    if (const int st = launch_dense_fmt(c.splits > 1, fmt, c.kind, p, g, s)) return st;  // before any launch
+    return launched("gemm");
+  });
+}
+
+// ---- scratch of the no-allocation entry point --------------------------------
+// Split-K arrival counters and partial sums of fp8_gemm_nt_noalloc live in
+// this file-scope device array: one copy per device, allocated when the
+// library's code is loaded on that device and held until the process ends.
+// In host code `scratch` only names the symbol; its device address on each
+// device comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is handed to kernels.  The
+// counters are tagged per call, so nothing in it needs clearing.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int noalloc_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return FP8G_ELAUNCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      if (log_enabled()) std::fprintf(stderr, "[fp8gemm] device %d: no address for the scratch array\n", dev);
+      return FP8G_ELAUNCH;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return FP8G_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -76,6 +161,7 @@ const char* fp8_status_string(int status) {
     case FP8G_EINVAL: return "invalid argument";
     case FP8G_EUNSUPPORTED: return "unsupported shape or layout";
     case FP8G_ELAUNCH: return "kernel launch failed";
+    case FP8G_ESCRATCH: return "problem needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
   }
 }
@@ -220,42 +306,34 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
 int fp8_gemm_nt_fmt(const uint8_t* lhs, int lhs_format, const float* lhs_scales, int64_t lhs_scales_ld,
                     const uint8_t* rhs, int rhs_format, const float* rhs_scales, uint16_t* out, int m, int n,
                     int k, void* workspace, size_t workspace_bytes, void* stream) {
-  if (m < 0) return FP8G_EINVAL;
-  if ((lhs_format != FP8G_E4M3 && lhs_format != FP8G_E5M2) || (rhs_format != FP8G_E4M3 && rhs_format != FP8G_E5M2))
-    return FP8G_EINVAL;
-  const int fmt = (lhs_format == FP8G_E5M2 ? 1 : 0) | (rhs_format == FP8G_E5M2 ? 2 : 0);
-  if (int st = check_gemm_shape(n, k)) return st;
+  int fmt = 0;
+  if (const int st = check_dense_args(lhs, lhs_format, lhs_scales, lhs_scales_ld, rhs, rhs_format, rhs_scales, out,
+                                      m, n, k, workspace, &fmt))
+    return st;
   if (m == 0 || n == 0) return FP8G_OK;
-  if (!lhs || !lhs_scales || !rhs || !rhs_scales || !out) return FP8G_EINVAL;
-  if (!aligned16(lhs) || !aligned16(lhs_scales) || !aligned16(rhs) || !aligned16(rhs_scales) ||
-      !aligned16(out) || (workspace && !aligned16(workspace)))
-    return FP8G_EINVAL;
-  if (int st = check_ld(lhs_scales_ld, m)) return st;
+  return run_dense_gemm(lhs, fmt, lhs_scales, lhs_scales_ld, rhs, rhs_scales, out, m, n, k, workspace,
+                        workspace_bytes, stream);
+}
 
-  DenseConfig c = dense_config(m, n, k, true);
-  if (c.splits > 1 && (!workspace || workspace_bytes < dense_workspace(c, m, n)))
-    c = dense_config(m, n, k, false);
-
-  GemmParams p{};
-  p.a = lhs; p.sa = lhs_scales; p.b = rhs; p.sb = rhs_scales; p.out = out;
-  if (c.splits > 1) {
-    p.tile_counters = static_cast<unsigned long long*>(workspace);
-    p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c));
-    p.epoch = next_epoch();
+int fp8_gemm_nt_noalloc(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld, const uint8_t* rhs,
+                        const float* rhs_scales, uint16_t* out, int m, int n, int k, void* stream) {
+  int fmt = 0;
+  if (const int st = check_dense_args(lhs, FP8G_E4M3, lhs_scales, lhs_scales_ld, rhs, FP8G_E4M3, rhs_scales, out, m,
+                                      n, k, nullptr, &fmt))
+    return st;
+  if (m == 0 || n == 0) return FP8G_OK;
+  // the configuration fp8_gemm_nt picks with a large enough workspace
+  const DenseConfig c = dense_config(m, n, k, true);
+  if (dense_workspace(c, m, n) > kNoAllocScratchBytes) {
+    if (log_enabled())
+      std::fprintf(stderr, "[fp8gemm] no-allocation GEMM m=%d n=%d k=%d needs %zu scratch bytes, above %zu\n", m, n,
+                   k, dense_workspace(c, m, n), kNoAllocScratchBytes);
+    return FP8G_ESCRATCH;
   }
-  p.sa_ld = lhs_scales_ld;
-  p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
-  p.tiles_m = c.tiles_m; p.tiles_n = c.tiles_n; p.splits = c.splits; p.groups_per_split = c.gps;
-  const int64_t grid = int64_t(c.tiles_m) * c.tiles_n * c.splits;
-  if (grid > 0x7fffffff) return FP8G_EUNSUPPORTED;
-  auto s = static_cast<hipStream_t>(stream);
-  if (log_enabled())
-    std::fprintf(stderr, "[fp8gemm] dense m=%d n=%d k=%d kind=%d tiles=%dx%d splits=%d grid=%lld\n", m, n, k,
-                 c.kind, c.tiles_m, c.tiles_n, c.splits, (long long)grid);
-  return launch_units(p, grid, [&](int64_t g) {
-    if (const int st = launch_dense_fmt(c.splits > 1, fmt, c.kind, p, g, s)) return st;  // before any launch
-    return launched("gemm");
-  });
+  void* ws = nullptr;
+  if (const int st = noalloc_scratch(&ws)) return st;
+  return run_dense_gemm(lhs, fmt, lhs_scales, lhs_scales_ld, rhs, rhs_scales, out, m, n, k, ws,
+                        kNoAllocScratchBytes, stream);
 }
 
 int fp8_grouped_gemm_contiguous(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,

@@ -51,7 +51,8 @@ enum {
   FP8G_OK = 0,
   FP8G_EINVAL = -1,
   FP8G_EUNSUPPORTED = -2,
-  FP8G_ELAUNCH = -3
+  FP8G_ELAUNCH = -3,
+  FP8G_ESCRATCH = -4  /* fp8_gemm_nt_noalloc: the problem needs more than its static scratch */
 };
 
 /* Element type of the cast helper's input. */
@@ -85,6 +86,25 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
                 const uint8_t* rhs, const float* rhs_scales,
                 uint16_t* out, int m, int n, int k,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp8_gemm_nt for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  It takes
+ * no workspace and allocates nothing; the split-K arrival counters and
+ * partial sums live in a static device array of 32 MiB inside the library
+ * (one per device, allocated when the library's code is loaded there and
+ * held until the process ends).  Same arguments, checks and configuration
+ * as fp8_gemm_nt with a large enough workspace, so the same bits.  A
+ * problem whose configuration needs more than 32 MiB of split-K scratch is
+ * refused with FP8G_ESCRATCH before anything is launched (on a 256-CU
+ * device the library's own configurations need at most about 16 MiB).
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents (nothing in it needs clearing: the arrival counters are
+ * tagged per call): calls that may overlap on one device -- other streams,
+ * other threads, other graphs in flight -- race on it and must be
+ * serialised (one stream) by the caller. */
+int fp8_gemm_nt_noalloc(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
+                        const uint8_t* rhs, const float* rhs_scales,
+                        uint16_t* out, int m, int n, int k, void* stream);
 
 /* Host only, launches nothing: writes a one-line description of the dense
  * configuration fp8_gemm_nt picks for (m, n, k) when the split-K workspace

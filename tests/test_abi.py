@@ -164,3 +164,14 @@ def test_split_override_only_where_split_k_can_run(lib, monkeypatch):
         assert binding.fp8_gemm_workspace_bytes(*shape) == 0
     assert "splits=4 " in d(64, 2112, 7168)          # the override itself works where split-K runs
     assert binding.fp8_gemm_workspace_bytes(64, 2112, 7168) > 0
+
+
+def test_noalloc_entry_point_host_checks(lib):
+    """fp8_gemm_nt_noalloc checks its arguments like fp8_gemm_nt, before it
+    looks up its scratch or launches anything."""
+    g = lib.fp8_gemm_nt_noalloc
+    assert g(None, None, 4, None, None, None, 4, 8, 128, None) == binding.FP8G_EINVAL
+    assert g(None, None, 4, None, None, None, -1, 8, 128, None) == binding.FP8G_EINVAL
+    assert g(None, None, 4, None, None, None, 4, 8, 100, None) == binding.FP8G_EUNSUPPORTED
+    assert g(None, None, 4, None, None, None, 0, 8, 128, None) == binding.FP8G_OK
+    assert "scratch" in binding.status_string(binding.FP8G_ESCRATCH)

@@ -200,11 +200,15 @@ int fp8_cast_per_token_group(const void* x, int x_dtype, int m, int k,
  * The fp8_jit_* GEMMs take the same arguments as the entry points above plus
  * a tile configuration (NULL: the one the ahead-of-time path would use).
  * The kernel for (configuration, operand formats, target, and n and k when
- * `specialize` is set) is compiled with hipRTC on first use, with the
- * device code-generation options of the library build, kept on disk in the
+ * `specialize` is set) is compiled on first use by the ROCm compiler run as
+ * a child process, with the device code-generation options of the library
+ * build, kept on disk in the
  * cache directory (default $FP8G_CACHE_DIR, else $HOME/.cache/fp8gemm) and
  * loaded once per device per process.  A cache file that does not match its
- * key, size or checksum is ignored, counted and replaced.  The first call
+ * key, size or checksum is ignored, counted and replaced.  A build that
+ * would need scratch memory (register spills) is refused with
+ * FP8G_EUNSUPPORTED, and the refusal is recorded in the cache, so later
+ * processes refuse it without compiling.  The first call
  * for a configuration therefore compiles (about a second) or reads the
  * disk; later calls only launch.  FP8G_JIT_DEBUG=1 reports compilations and
  * cache use on stderr; FP8G_JIT_COMPILER names the compiler (default
@@ -223,7 +227,11 @@ typedef struct fp8_gemm_config {
   int waves_m;      /* wave grid over the tile: waves_m * waves_n * waves_k is 4 or 8; */
   int waves_n;      /*   each wave's share is a multiple of 16 by 16, at most 32 MFMA */
   int waves_k;      /*   tiles, and its n range divides 128 */
-  int stages;       /* LDS ring stages, 2..8 */
+  int stages;       /* LDS ring stages, 1..8; 1 is the single-buffer debug form
+                       ("DeepGEMM: FP8 GEMM kernel optimisation practice on
+                       Hopper Tensor Cores", section 6.2): no copy overlaps
+                       the products.  FP8G_PIPELINE_DEPTH=d sets every
+                       configuration's stages to d. */
   int k_per_stage;  /* 128-wide K groups per stage, 1..4, a multiple of waves_k */
   int splits;       /* split-K workgroups per tile, 1..8 (dense only; grouped: 1) */
   int specialize;   /* nonzero: n and k are compiled in */

@@ -125,7 +125,7 @@ int run_dense_gemm(const uint8_t* lhs, int fmt, const float* lhs_scales, int64_t
 // device current, and only that address is handed to kernels.  The
 // counters are tagged per call, so nothing in it needs clearing.
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
-__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;

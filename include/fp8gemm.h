@@ -101,7 +101,9 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
  * call's contents (nothing in it needs clearing: the arrival counters are
  * tagged per call): calls that may overlap on one device -- other streams,
  * other threads, other graphs in flight -- race on it and must be
- * serialised (one stream) by the caller. */
+ * serialised (one stream) by the caller.  The first call on a device looks
+ * up the array's device address (no allocation and no stream operation);
+ * make one call before capturing the entry point in a HIP graph. */
 int fp8_gemm_nt_noalloc(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
                         const uint8_t* rhs, const float* rhs_scales,
                         uint16_t* out, int m, int n, int k, void* stream);

@@ -104,27 +104,57 @@ __device__ __forceinline__ void copy4_to_lds(const void* sbase, uint32_t voffset
                :: "s"(uniform(int(lds_wave_base))), "v"(voffset), "s"(uniform_ptr(sbase)) : "memory");
 }
 
-// Device-coherent 16-byte global store / load (sc1: past the per-XCD L2s, so
-// another XCD sees the data once the access has completed).  Used for split-K
+// Device-coherent 16-byte global store (sc1: past the per-XCD L2s, so
+// another XCD sees the data once the store has completed).  Used for split-K
 // partial sums that another workgroup, possibly on another XCD, adds up.
-// The load waits for its own data.
 __device__ __forceinline__ void store16_coherent(float* p, const v4f& v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" :: "v"(p), "v"(v) : "memory");
 }
-// Issue only: the data may be used after wait_coherent() has returned it.
-__device__ __forceinline__ v4f load16_coherent_issue(const float* p) {
-  v4f v;
-  asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-  return v;
+// S device-coherent 16-byte loads, t[i] = *q[i], issued together and waited
+// for (vmcnt(0)) inside one assembly statement: no register of a load still
+// in flight is ever visible to the compiler, so it can neither read nor
+// reuse one early.  The early-clobber outputs keep every destination apart
+// from the addresses of the loads after it.
+#define FP8G_LDC(o, i) "global_load_dwordx4 %" #o ", %" #i ", off sc1\n\t"
+template <int S>
+__device__ __forceinline__ void load16_coherent(const float* const (&q)[S], v4f (&t)[S]) {
+  static_assert(S >= 1 && S <= 8, "one to eight loads");
+  if constexpr (S == 1) {
+    asm volatile(FP8G_LDC(0, 1) "s_waitcnt vmcnt(0)" : "=&v"(t[0]) : "v"(q[0]) : "memory");
+  } else if constexpr (S == 2) {
+    asm volatile(FP8G_LDC(0, 2) FP8G_LDC(1, 3) "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]) : "v"(q[0]), "v"(q[1]) : "memory");
+  } else if constexpr (S == 3) {
+    asm volatile(FP8G_LDC(0, 3) FP8G_LDC(1, 4) FP8G_LDC(2, 5) "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]) : "v"(q[0]), "v"(q[1]), "v"(q[2]) : "memory");
+  } else if constexpr (S == 4) {
+    asm volatile(FP8G_LDC(0, 4) FP8G_LDC(1, 5) FP8G_LDC(2, 6) FP8G_LDC(3, 7) "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3])
+                 : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]) : "memory");
+  } else if constexpr (S == 5) {
+    asm volatile(FP8G_LDC(0, 5) FP8G_LDC(1, 6) FP8G_LDC(2, 7) FP8G_LDC(3, 8) FP8G_LDC(4, 9) "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4])
+                 : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]) : "memory");
+  } else if constexpr (S == 6) {
+    asm volatile(FP8G_LDC(0, 6) FP8G_LDC(1, 7) FP8G_LDC(2, 8) FP8G_LDC(3, 9) FP8G_LDC(4, 10) FP8G_LDC(5, 11)
+                 "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5])
+                 : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]) : "memory");
+  } else if constexpr (S == 7) {
+    asm volatile(FP8G_LDC(0, 7) FP8G_LDC(1, 8) FP8G_LDC(2, 9) FP8G_LDC(3, 10) FP8G_LDC(4, 11) FP8G_LDC(5, 12)
+                 FP8G_LDC(6, 13) "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6])
+                 : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]) : "memory");
+  } else {
+    asm volatile(FP8G_LDC(0, 8) FP8G_LDC(1, 9) FP8G_LDC(2, 10) FP8G_LDC(3, 11) FP8G_LDC(4, 12) FP8G_LDC(5, 13)
+                 FP8G_LDC(6, 14) FP8G_LDC(7, 15) "s_waitcnt vmcnt(0)"
+                 : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]), "=&v"(t[3]), "=&v"(t[4]), "=&v"(t[5]), "=&v"(t[6]),
+                   "=&v"(t[7])
+                 : "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]), "v"(q[4]), "v"(q[5]), "v"(q[6]), "v"(q[7])
+                 : "memory");
+  }
 }
-// Waits for every outstanding vector-memory access; the values pass through
-// the statement, so no use of them can be scheduled before the wait.
-__device__ __forceinline__ void wait_coherent(v4f (&t)[8]) {
-  asm volatile("s_waitcnt vmcnt(0)"
-               : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]), "+v"(t[4]), "+v"(t[5]), "+v"(t[6]), "+v"(t[7])
-               :: "memory");
-}
-
+#undef FP8G_LDC
 
 // FP8 formats of the operands (the f8f6f4 MFMA's per-operand format codes).
 constexpr int kFmtE4M3 = 0, kFmtE5M2 = 1;

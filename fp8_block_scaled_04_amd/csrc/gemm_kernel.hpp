@@ -34,6 +34,7 @@ enum GemmMode { kDense = 0, kContiguous = 1, kMasked = 2 };
 
 constexpr int kXcds = 8;    // XCDs of an MI355X; workgroups are dealt to them round-robin
 constexpr int kGroupM = 4;  // M-tiles walked together in the dense tile order
+constexpr int kMaxSplits = 8;  // split-K partials the fix-up adds at most
 
 struct GemmParams {
   const uint8_t* a;          // LHS codes
@@ -701,13 +702,19 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
                          *reinterpret_cast<const v4f*>(stage + r * LDT + c4));
     }
     __shared__ int last_arrival;
+    // counter word: epoch in the high 32 bits, arrivals in the low 32; a
+    // word from another call (or uninitialised memory) restarts the count.
+    // Its current value is fetched while the partial's stores are still in
+    // flight: it only seeds the compare-and-swap below, which re-reads the
+    // word whenever it has changed, and the arrival itself is counted after
+    // every store has completed.
+    unsigned long long* ctr = p.tile_counters + (int64_t(m_tile) * p.tiles_n + n_tile);
+    unsigned long long seen = 0;
+    if (threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     wait_vmcnt<0>();
     __syncthreads();
     if (threadIdx.x == 0) {
-      // counter word: epoch in the high 32 bits, arrivals in the low 32; a
-      // word from another call (or uninitialised memory) restarts the count
-      unsigned long long* ctr = p.tile_counters + (int64_t(m_tile) * p.tiles_n + n_tile);
-      unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      unsigned long long old = seen;
       unsigned long long nxt;
       do {
         nxt = (unsigned(old >> 32) == p.epoch) ? old + 1 : ((unsigned long long)p.epoch << 32) | 1ull;
@@ -719,26 +726,40 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     }
     __syncthreads();
     if (!last_arrival) return;
-    // all splits of a chunk are requested before one wait (kMaxSplits <= 8)
-    for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
-      const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
-      if (m0 + r < rows && n0 + c4 < shape_n) {
-        const float* P = p.partial + int64_t(m0 + r) * shape_n + n0 + c4;
-        const v4f mine = *reinterpret_cast<const v4f*>(stage + r * LDT + c4);
-        v4f t[8];
+    // Every split's partial of a 4-wide chunk (this one's too, read back
+    // like the others) is requested before one wait, then added in split
+    // order.
+    auto add_partials = [&](auto s_tag) {
+      constexpr int S = decltype(s_tag)::value;
+      for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
+        const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
+        if (m0 + r < rows && n0 + c4 < shape_n) {
+          const float* P = p.partial + int64_t(m0 + r) * shape_n + n0 + c4;
+          const float* q[S];
 #pragma unroll
-        for (int sp = 0; sp < 8; ++sp)
-          t[sp] = (sp < p.splits && sp != split) ? load16_coherent_issue(P + sp * mn) : mine;
-        wait_coherent(t);
-        v4f sum = t[0];
+          for (int sp = 0; sp < S; ++sp) q[sp] = P + sp * mn;
+          v4f t[S];
+          load16_coherent<S>(q, t);
+          v4f sum = t[0];
 #pragma unroll
-        for (int sp = 1; sp < 8; ++sp)
-          if (sp < p.splits) sum += t[sp];
-        uint2 v;
-        v.x = pack_bf16x2(sum[0], sum[1]);
-        v.y = pack_bf16x2(sum[2], sum[3]);
-        *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * shape_n + n0 + c4) = v;
+          for (int sp = 1; sp < S; ++sp) sum += t[sp];
+          uint2 v;
+          v.x = pack_bf16x2(sum[0], sum[1]);
+          v.y = pack_bf16x2(sum[2], sum[3]);
+          *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * shape_n + n0 + c4) = v;
+        }
       }
+    };
+    static_assert(kMaxSplits == 8, "one case per split count");
+    switch (p.splits) {
+      case 1: add_partials(Int<1>{}); break;
+      case 2: add_partials(Int<2>{}); break;
+      case 3: add_partials(Int<3>{}); break;
+      case 4: add_partials(Int<4>{}); break;
+      case 5: add_partials(Int<5>{}); break;
+      case 6: add_partials(Int<6>{}); break;
+      case 7: add_partials(Int<7>{}); break;
+      default: add_partials(Int<8>{}); break;
     }
   } else {
     // The tile goes out through LDS: a lane's accumulators are 4 columns of

@@ -12,6 +12,7 @@
 #include <cstdlib>
 
 #include "fp8gemm.h"
+#include "gemm_kernel.hpp"  // kMaxSplits, kMaxGroups
 
 namespace fp8g {
 namespace host {
@@ -114,7 +115,6 @@ constexpr int kSmallFamilies[] = {kF64N32, kF64N64, kF64N128, kF128N128};
 // 128 x 128 on 16 slots of 256 rows holding U{0..256} tokens each).
 constexpr KernelShape kContiguousShape = {256, 256, 2, 8, 1, 4, 2, 1};
 constexpr KernelShape kMaskedShape = {64, 128, 3, 4, 1, 1, 4, 1};
-constexpr int kMaxSplits = 8;  // the split-K fix-up adds at most this many partials
 
 struct DenseConfig {
   int kind, tiles_m, tiles_n, splits, gps;

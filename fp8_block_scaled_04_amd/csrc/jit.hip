@@ -177,7 +177,7 @@ bool valid_config(const fp8_gemm_config& c, int mode) {
   const int tm = wm / 16, tn = wn / 16;
   if (tm * tn > 32) return false;  // accumulators stay within 128 VGPRs
   if (c.waves_k > 1 && nw * tn * tm * 64 * 16 > ring) return false;
-  if (c.splits < 1 || c.splits > kMaxSplits) return false;
+  if (c.splits < 1 || c.splits > fp8g::kMaxSplits) return false;
   if (c.splits > 1 && mode != FP8G_JIT_DENSE) return false;
   if (mode == FP8G_JIT_CONTIGUOUS && c.block_m != 256) return false;
   return mode == FP8G_JIT_DENSE || mode == FP8G_JIT_CONTIGUOUS || mode == FP8G_JIT_MASKED;

@@ -399,6 +399,144 @@ __device__ __forceinline__ bool masked_unit(const int32_t* masked_m, int groups,
   return false;  // not reached: L < total
 }
 
+// ---- epilogue ---------------------------------------------------------------
+// Writes a workgroup's BM x BN tile from the accumulators of the waves that
+// hold it (holder): wave (wrow_m, wrow_n) holds tokens wrow_m.. and outputs
+// wrow_n.. of the tile as acc[i][j] = sub-tile (n 16 i.., token 16 j..), each
+// lane 4 consecutive n of one token.  smem (at least epilogue_lds<BM, BN>(SPLIT)
+// bytes, free once the K loop is done) stages the tile.  Every thread of the
+// workgroup calls it.
+template <int BM, int BN>
+constexpr int epilogue_lds(bool split) {
+  return split ? BM * (BN + 4) * 4 : BM * (BN + 8) * 2;
+}
+
+template <int BM, int BN, int TM, int TN, bool SPLIT>
+__device__ __forceinline__ void write_tile(const GemmParams& p, const v4f (&acc)[TN][TM], uint8_t* smem, bool holder,
+                                           int wrow_m, int wrow_n, int m0, int n0, int rows, int shape_n, int split,
+                                           int m_tile, int n_tile, uint16_t* OUT) {
+  const int lane = threadIdx.x & (kWave - 1);
+  constexpr int OUT_LDT = BN + 8;  // padded row stride (elements) of the staged BF16 tile
+  if constexpr (SPLIT) {
+    // Publish this split's partial tile, then count arrivals on the tile.
+    // The last workgroup to arrive adds all partials in split order
+    // (p_0 + p_1 + ... + p_{S-1}), so the result does not depend on arrival
+    // order.  The tile is staged through LDS (free once the K loop is done)
+    // so that partials move as whole rows of 16-byte device-coherent
+    // accesses, which go past the per-XCD L2s: retiring the stores before
+    // the arrival is counted makes them visible to the last workgroup
+    // without any cache-wide write-back or invalidate.
+    constexpr int LDT = BN + 4;  // padded row stride (floats) of the staged tile
+    constexpr int CHUNKS = BM * BN / 4;
+    float* stage = reinterpret_cast<float*>(smem);
+    __syncthreads();  // every wave is done with the ring (and with the partial-tile sums)
+    if (holder) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j)
+          *reinterpret_cast<v4f*>(stage + (wrow_m + 16 * j + (lane & 15)) * LDT + wrow_n + 16 * i + 4 * (lane >> 4)) =
+              acc[i][j];
+    }
+    __syncthreads();
+    const int64_t mn = int64_t(p.m) * shape_n;
+    for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
+      const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
+      if (m0 + r < rows && n0 + c4 < shape_n)
+        store16_coherent(p.partial + split * mn + int64_t(m0 + r) * shape_n + n0 + c4,
+                         *reinterpret_cast<const v4f*>(stage + r * LDT + c4));
+    }
+    __shared__ int last_arrival;
+    // counter word: epoch in the high 32 bits, arrivals in the low 32; a
+    // word from another call (or uninitialised memory) restarts the count.
+    // Its current value is fetched while the partial's stores are still in
+    // flight: it only seeds the compare-and-swap below, which re-reads the
+    // word whenever it has changed, and the arrival itself is counted after
+    // every store has completed.
+    unsigned long long* ctr = p.tile_counters + (int64_t(m_tile) * p.tiles_n + n_tile);
+    unsigned long long seen = 0;
+    if (threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      unsigned long long old = seen;
+      unsigned long long nxt;
+      do {
+        nxt = (unsigned(old >> 32) == p.epoch) ? old + 1 : ((unsigned long long)p.epoch << 32) | 1ull;
+      } while (!__hip_atomic_compare_exchange_strong(ctr, &old, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT));
+      const bool last = unsigned(nxt) == unsigned(p.splits);
+      if (last) __hip_atomic_store(ctr, (unsigned long long)p.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_arrival = last;
+    }
+    __syncthreads();
+    if (!last_arrival) return;
+    // Every split's partial of a 4-wide chunk (this one's too, read back
+    // like the others) is requested before one wait, then added in split
+    // order.
+    auto add_partials = [&](auto s_tag) {
+      constexpr int S = decltype(s_tag)::value;
+      for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
+        const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
+        if (m0 + r < rows && n0 + c4 < shape_n) {
+          const float* P = p.partial + int64_t(m0 + r) * shape_n + n0 + c4;
+          const float* q[S];
+#pragma unroll
+          for (int sp = 0; sp < S; ++sp) q[sp] = P + sp * mn;
+          v4f t[S];
+          load16_coherent<S>(q, t);
+          v4f sum = t[0];
+#pragma unroll
+          for (int sp = 1; sp < S; ++sp) sum += t[sp];
+          uint2 v;
+          v.x = pack_bf16x2(sum[0], sum[1]);
+          v.y = pack_bf16x2(sum[2], sum[3]);
+          *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * shape_n + n0 + c4) = v;
+        }
+      }
+    };
+    static_assert(kMaxSplits == 8, "one case per split count");
+    switch (p.splits) {
+      case 1: add_partials(Int<1>{}); break;
+      case 2: add_partials(Int<2>{}); break;
+      case 3: add_partials(Int<3>{}); break;
+      case 4: add_partials(Int<4>{}); break;
+      case 5: add_partials(Int<5>{}); break;
+      case 6: add_partials(Int<6>{}); break;
+      case 7: add_partials(Int<7>{}); break;
+      default: add_partials(Int<8>{}); break;
+    }
+  } else {
+    // The tile goes out through LDS: a lane's accumulators are 4 columns of
+    // one row per sub-tile, so stored directly each instruction would write
+    // 32 bytes into each of 16 rows; staged, every instruction writes whole
+    // rows in 16-byte pieces (measured: the output burst at the end of a
+    // round of large-M tiles drains about twice as fast).
+    uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
+    __syncthreads();  // every wave is done with the ring (and with the partial-tile sums)
+    if (holder) {
+#pragma unroll
+      for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          *reinterpret_cast<uint2*>(stage + (wrow_m + 16 * j + (lane & 15)) * OUT_LDT + wrow_n + 16 * i +
+                                    4 * (lane >> 4)) = v;
+        }
+    }
+    __syncthreads();
+    constexpr int CHUNKS = BN / 8;  // 16-byte pieces per tile row (n % 8 == 0: a piece is all in or all out)
+    for (int c = threadIdx.x; c < BM * CHUNKS; c += blockDim.x) {
+      const int r = c / CHUNKS, col = n0 + 8 * (c % CHUNKS);
+      if (m0 + r < rows && col < shape_n)
+        *reinterpret_cast<uint4*>(OUT + int64_t(m0 + r) * shape_n + col) =
+            *reinterpret_cast<const uint4*>(stage + r * OUT_LDT + 8 * (c % CHUNKS));
+    }
+  }
+}
+
 // KU consecutive K groups share one ring stage (one wait and one barrier),
 // and WK waves (dividing KU) may share each sub-tile, taking every WK-th
 // group of a stage; their partial tiles are added in LDS, in wave order,
@@ -442,11 +580,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   // (rows padded by 8 elements so that neither the fragment-ordered writes
   // nor the row-ordered reads pile onto a few banks).
   // A split's FP32 partial tile is staged the same way (rows padded by 4).
-  constexpr int OUT_LDT = BN + 8;
-  constexpr int OUT_BYTES = BM * OUT_LDT * 2;
-  constexpr int PART_BYTES = SPLIT ? BM * (BN + 4) * 4 : 0;
-  constexpr int SMEM = RING > OUT_BYTES ? (RING > PART_BYTES ? RING : PART_BYTES)
-                                        : (OUT_BYTES > PART_BYTES ? OUT_BYTES : PART_BYTES);
+  constexpr int EPI = epilogue_lds<BM, BN>(SPLIT);
+  constexpr int SMEM = RING > EPI ? RING : EPI;
   static_assert(SMEM + SB_BLOCKS * kMaxGroups * 4 <= 160 * 1024, "LDS with the output staging");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
   __shared__ float sb_cache[SB_BLOCKS][kMaxGroups];
@@ -669,127 +804,8 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     }
   }
   const bool holder = wk == 0;  // the waves that now hold the tile's sums
-
-  // ---- epilogue: lane holds n = col..col+3 of one token per sub-tile -------
-  if constexpr (SPLIT) {
-    // Publish this split's partial tile, then count arrivals on the tile.
-    // The last workgroup to arrive adds all partials in split order
-    // (p_0 + p_1 + ... + p_{S-1}), so the result does not depend on arrival
-    // order.  The tile is staged through LDS (free once the K loop is done)
-    // so that partials move as whole rows of 16-byte device-coherent
-    // accesses, which go past the per-XCD L2s: retiring the stores before
-    // the arrival is counted makes them visible to the last workgroup
-    // without any cache-wide write-back or invalidate.
-    static_assert(BM * (BN + 4) * 4 <= SMEM, "staged partial tile fits");
-    constexpr int LDT = BN + 4;  // padded row stride (floats) of the staged tile
-    constexpr int CHUNKS = BM * BN / 4;
-    float* stage = reinterpret_cast<float*>(smem);
-    __syncthreads();  // every wave is done with the ring (and with the partial-tile sums)
-    if (holder) {
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j)
-          *reinterpret_cast<v4f*>(stage + (wrow_m + 16 * j + (lane & 15)) * LDT + wrow_n + 16 * i + 4 * (lane >> 4)) =
-              acc[i][j];
-    }
-    __syncthreads();
-    const int64_t mn = int64_t(p.m) * shape_n;
-    for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
-      const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
-      if (m0 + r < rows && n0 + c4 < shape_n)
-        store16_coherent(p.partial + split * mn + int64_t(m0 + r) * shape_n + n0 + c4,
-                         *reinterpret_cast<const v4f*>(stage + r * LDT + c4));
-    }
-    __shared__ int last_arrival;
-    // counter word: epoch in the high 32 bits, arrivals in the low 32; a
-    // word from another call (or uninitialised memory) restarts the count.
-    // Its current value is fetched while the partial's stores are still in
-    // flight: it only seeds the compare-and-swap below, which re-reads the
-    // word whenever it has changed, and the arrival itself is counted after
-    // every store has completed.
-    unsigned long long* ctr = p.tile_counters + (int64_t(m_tile) * p.tiles_n + n_tile);
-    unsigned long long seen = 0;
-    if (threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      unsigned long long old = seen;
-      unsigned long long nxt;
-      do {
-        nxt = (unsigned(old >> 32) == p.epoch) ? old + 1 : ((unsigned long long)p.epoch << 32) | 1ull;
-      } while (!__hip_atomic_compare_exchange_strong(ctr, &old, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
-      const bool last = unsigned(nxt) == unsigned(p.splits);
-      if (last) __hip_atomic_store(ctr, (unsigned long long)p.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      last_arrival = last;
-    }
-    __syncthreads();
-    if (!last_arrival) return;
-    // Every split's partial of a 4-wide chunk (this one's too, read back
-    // like the others) is requested before one wait, then added in split
-    // order.
-    auto add_partials = [&](auto s_tag) {
-      constexpr int S = decltype(s_tag)::value;
-      for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
-        const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
-        if (m0 + r < rows && n0 + c4 < shape_n) {
-          const float* P = p.partial + int64_t(m0 + r) * shape_n + n0 + c4;
-          const float* q[S];
-#pragma unroll
-          for (int sp = 0; sp < S; ++sp) q[sp] = P + sp * mn;
-          v4f t[S];
-          load16_coherent<S>(q, t);
-          v4f sum = t[0];
-#pragma unroll
-          for (int sp = 1; sp < S; ++sp) sum += t[sp];
-          uint2 v;
-          v.x = pack_bf16x2(sum[0], sum[1]);
-          v.y = pack_bf16x2(sum[2], sum[3]);
-          *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * shape_n + n0 + c4) = v;
-        }
-      }
-    };
-    static_assert(kMaxSplits == 8, "one case per split count");
-    switch (p.splits) {
-      case 1: add_partials(Int<1>{}); break;
-      case 2: add_partials(Int<2>{}); break;
-      case 3: add_partials(Int<3>{}); break;
-      case 4: add_partials(Int<4>{}); break;
-      case 5: add_partials(Int<5>{}); break;
-      case 6: add_partials(Int<6>{}); break;
-      case 7: add_partials(Int<7>{}); break;
-      default: add_partials(Int<8>{}); break;
-    }
-  } else {
-    // The tile goes out through LDS: a lane's accumulators are 4 columns of
-    // one row per sub-tile, so stored directly each instruction would write
-    // 32 bytes into each of 16 rows; staged, every instruction writes whole
-    // rows in 16-byte pieces (measured: the output burst at the end of a
-    // round of large-M tiles drains about twice as fast).
-    uint16_t* stage = reinterpret_cast<uint16_t*>(smem);
-    __syncthreads();  // every wave is done with the ring (and with the partial-tile sums)
-    if (holder) {
-#pragma unroll
-      for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) {
-          uint2 v;
-          v.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-          v.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-          *reinterpret_cast<uint2*>(stage + (wrow_m + 16 * j + (lane & 15)) * OUT_LDT + wrow_n + 16 * i +
-                                    4 * (lane >> 4)) = v;
-        }
-    }
-    __syncthreads();
-    constexpr int CHUNKS = BN / 8;  // 16-byte pieces per tile row (n % 8 == 0: a piece is all in or all out)
-    for (int c = threadIdx.x; c < BM * CHUNKS; c += blockDim.x) {
-      const int r = c / CHUNKS, col = n0 + 8 * (c % CHUNKS);
-      if (m0 + r < rows && col < shape_n)
-        *reinterpret_cast<uint4*>(OUT + int64_t(m0 + r) * shape_n + col) =
-            *reinterpret_cast<const uint4*>(stage + r * OUT_LDT + 8 * (c % CHUNKS));
-    }
-  }
+  write_tile<BM, BN, TM, TN, SPLIT>(p, acc, smem, holder, wrow_m, wrow_n, m0, n0, rows, shape_n, split, m_tile, n_tile,
+                                    OUT);
 }
 
 }  // namespace fp8g

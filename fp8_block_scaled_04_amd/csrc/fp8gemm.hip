@@ -401,7 +401,8 @@ int fp8_grouped_gemm_masked(const uint8_t* lhs, const float* lhs_scales, int64_t
     std::fprintf(stderr, "[fp8gemm] masked G=%d max_m=%d n=%d k=%d grid=%lld\n", num_groups, max_m, n, k,
                  (long long)grid);
   return launch_units(p, grid, [&](int64_t g) {
-    launch_gemm<64, 128, 1, 4, 3, kMasked, false>(p, g, static_cast<hipStream_t>(stream));
+    launch_gemm<kMaskedShape.bm, kMaskedShape.bn, kMaskedShape.wm, kMaskedShape.wn, kMaskedShape.stages, kMasked,
+                false>(p, g, static_cast<hipStream_t>(stream));
     return launched("masked gemm");
   });
 }

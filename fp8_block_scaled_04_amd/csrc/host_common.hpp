@@ -110,11 +110,14 @@ constexpr KernelShape kShapes[kKinds] = {
 };
 constexpr int kSmallFamilies[] = {kF64N32, kF64N64, kF64N128, kF128N128};
 // The grouped kernels' shapes: contiguous 256 x 256 tiles (one or two
-// 128-row blocks of one group); masked 64 x 128 tiles, so that slots that
-// are mostly empty (decode) waste few rows (measured: 12% faster than
-// 128 x 128 on 16 slots of 256 rows holding U{0..256} tokens each).
+// 128-row blocks of one group); masked 64-row tiles, so that slots that are
+// mostly empty (decode) waste few rows (measured on 16 slots of 256 rows
+// holding U{0..256} tokens each: 64 x 128 was 12% faster than 128 x 128,
+// and 64 x 256 with 2 x 4 waves and three stages 2-4% faster than 64 x 128,
+// alternated four times on one box: the wider tile copies the shared LHS
+// rows once per 256 outputs instead of once per 128).
 constexpr KernelShape kContiguousShape = {256, 256, 2, 8, 1, 4, 2, 1};
-constexpr KernelShape kMaskedShape = {64, 128, 3, 4, 1, 1, 4, 1};
+constexpr KernelShape kMaskedShape = {64, 256, 3, 8, 1, 2, 4, 1};
 
 struct DenseConfig {
   int kind, tiles_m, tiles_n, splits, gps;

@@ -56,7 +56,7 @@ def test_default_config_is_the_ahead_of_time_choice(lib):
         assert c.waves_m * c.waves_n * c.waves_k == int(text.split("waves=")[1].split()[0])
         assert binding.fp8_jit_config_supported(D, c)
     assert binding.fp8_jit_default_config(C, 1, 4096, 7168).block_m == 256
-    assert binding.fp8_jit_default_config(M, 1, 4096, 7168).as_dict() == cfg(block_m=64, waves_m=1, waves_n=4)
+    assert binding.fp8_jit_default_config(M, 1, 4096, 7168).as_dict() == cfg(block_m=64, block_n=256, waves_m=2, waves_n=4)
     for mode in (C, M):
         assert binding.fp8_jit_config_supported(mode, binding.fp8_jit_default_config(mode, 1, 4096, 7168))
     with pytest.raises(binding.Fp8GemmError):

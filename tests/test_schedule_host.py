@@ -137,7 +137,8 @@ def test_contiguous_every_tile_exactly_once(lib):
 
 def test_masked_every_live_unit_exactly_once(lib):
     rng = np.random.default_rng(11)
-    bm, bn = 64, 128                          # the masked kernel's tile
+    tile = binding.fp8_jit_default_config(MASKED, 1, 1024, 128)  # the masked kernel's tile
+    bm, bn = tile.block_m, tile.block_n
     for case in range(CASES):
         lim = cu_limit(rng)
         binding.fp8_set_num_cus(lim)

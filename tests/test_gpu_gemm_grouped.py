@@ -40,6 +40,22 @@ def test_contiguous_skipped_block_untouched():
     assert_close(got[valid], ref[valid], "contiguous with a skipped block")
 
 
+def test_grouped_with_nothing_to_do_writes_nothing():
+    """Degenerate group data: every 128-row block skipped (contiguous), and
+    every count zero or negative (masked).  Neither kernel has a unit with
+    work, so every workgroup exits and the output (and its canary bands)
+    keep the sentinel."""
+    require_gpu()
+    n, k = 264, 256
+    qa, sa, qb, sb, m_idx = contiguous_case([256, 128], n, k, seed=3)
+    say("contiguous, every block skipped")
+    assert np.all(run_contiguous(qa, sa, qb, sb, np.full_like(m_idx, -1)) == SENTINEL)
+    G, max_m = 5, 96
+    say("masked, every count zero or negative")
+    qa, sa, qb, sb = masked_case(G, max_m, n, k, [0] * G, seed=4)
+    assert np.all(run_masked(qa, sa, qb, sb, [0, -4, 0, 0, -1]) == SENTINEL)
+
+
 @pytest.mark.parametrize("pattern", ["odd_runs", "skip_inside_run", "interleaved", "many_blocks"])
 def test_contiguous_tiling_patterns(pattern):
     """Group runs of odd block counts (one-block tiles), a run cut by a

@@ -268,7 +268,7 @@ int fp8_gemm_schedule(int mode, int m, int n, int k, int num_groups, const int32
       const int bid = int(b) + p.unit_offset;
       if (mode == FP8G_JIT_DENSE) {
         int mt, nt, sp;
-        dense_tile(xcd_logical(bid, p.units), p.tiles_m, p.tiles_n, p.splits, mt, nt, sp);
+        dense_tile(p.unit_offset + xcd_logical(int(b), int(g)), p.tiles_m, p.tiles_n, p.splits, mt, nt, sp);
         record(1, 0, mt * bm, std::min(bm, m - mt * bm), nt, sp);
       } else if (mode == FP8G_JIT_CONTIGUOUS) {
         if (bid >= contig_tiles * p.tiles_n) { record(0, -1, 0, 0, 0, 0); continue; }

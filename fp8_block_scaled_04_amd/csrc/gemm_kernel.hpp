@@ -601,7 +601,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
   // ---- work unit ------------------------------------------------------
   // Unit blockIdx.x + p.unit_offset of p.units: a launch covers all units,
   // or, under a CU limit, one of several consecutive slices of them.
-  const int bid = blockIdx.x + p.unit_offset;
+  [[maybe_unused]] const int bid = blockIdx.x + p.unit_offset;
   int split = 0;
   int n_tile, m_tile, group = 0;
   int tiles_m = p.tiles_m;
@@ -613,10 +613,17 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N * WK, 1) gemm_kernel(co
     tiles_m = cs.tiles;
     if (bid >= tiles_m * p.tiles_n) return;
   }
-  if constexpr (MODE == kDense || MODE == kContiguous) {
-    // (every workgroup below the unit count has a unit: bid < total)
-    const int L = xcd_logical(bid, MODE == kContiguous ? tiles_m * p.tiles_n : p.units);
+  if constexpr (MODE == kDense) {
+    // Each launch deals its own units [unit_offset, unit_offset + gridDim.x)
+    // to the XCDs (all of them when there is no CU limit), so that every
+    // slice of a CU-limited call also keeps the tiles that run together on
+    // one XCD; every workgroup of the launch has a unit.
+    const int L = p.unit_offset + xcd_logical(blockIdx.x, gridDim.x);
     dense_tile(L, tiles_m, p.tiles_n, SPLIT ? p.splits : 1, m_tile, n_tile, split);
+  } else if constexpr (MODE == kContiguous) {
+    // (every workgroup below the tile count has a unit: bid < total)
+    const int L = xcd_logical(bid, tiles_m * p.tiles_n);
+    dense_tile(L, tiles_m, p.tiles_n, 1, m_tile, n_tile, split);
   } else {
     // (p.units counts every possible unit: groups x tiles_m x tiles_n)
     if (!masked_unit<BM>(p.masked_m, p.units / (p.tiles_m * p.tiles_n), p.m, p.tiles_n, bid, group,

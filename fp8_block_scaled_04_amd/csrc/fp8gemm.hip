@@ -99,7 +99,7 @@ int run_dense_gemm(const uint8_t* lhs, int fmt, const float* lhs_scales, int64_t
   if (c.splits > 1) {
     p.tile_counters = static_cast<unsigned long long*>(workspace);
     p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(c));
-    p.epoch = next_epoch();
+    p.tag = counter_tag();
   }
   p.sa_ld = lhs_scales_ld;
   p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));
@@ -123,7 +123,7 @@ int run_dense_gemm(const uint8_t* lhs, int fmt, const float* lhs_scales, int64_t
 // In host code `scratch` only names the symbol; its device address on each
 // device comes from hipGetSymbolAddress, taken once per device with that
 // device current, and only that address is handed to kernels.  The
-// counters are tagged per call, so nothing in it needs clearing.
+// counters carry a tag, so nothing in it needs clearing.
 constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 

@@ -44,7 +44,7 @@ struct GemmParams {
   uint16_t* out;             // BF16 output
   float* partial;            // split-K partial sums [splits][m][n] (dense only)
   unsigned long long* tile_counters;  // split-K arrival counters, one per output tile
-  unsigned int epoch;        // this call's tag for the arrival counters (never 0)
+  unsigned int tag;          // tag of the split-K arrival counters (never 0)
   const int32_t* m_indices;  // contiguous: group of each row
   const int32_t* masked_m;   // masked: valid rows per group
   int64_t sa_ld;
@@ -447,12 +447,17 @@ __device__ __forceinline__ void write_tile(const GemmParams& p, const v4f (&acc)
                          *reinterpret_cast<const v4f*>(stage + r * LDT + c4));
     }
     __shared__ int last_arrival;
-    // counter word: epoch in the high 32 bits, arrivals in the low 32; a
-    // word from another call (or uninitialised memory) restarts the count.
-    // Its current value is fetched while the partial's stores are still in
-    // flight: it only seeds the compare-and-swap below, which re-reads the
-    // word whenever it has changed, and the arrival itself is counted after
-    // every store has completed.
+    // counter word: tag in the high 32 bits, arrivals in the low 32.  The
+    // last arrival leaves the word at (tag, 0), so a word carrying this
+    // call's tag counts arrivals from zero, and nothing but this call's
+    // arrivals touches it (calls sharing a workspace run one after
+    // another): a fetch-and-add counts the arrival in one round trip.  A
+    // word with another tag (uninitialised memory, partial sums of another
+    // configuration, a counter left by a launch that failed part-way) is
+    // replaced by (tag, 1) with a compare-and-swap, which, if some other
+    // arrival got there first, returns the word as it now is.  The word is
+    // fetched while the partial's stores are still in flight; the arrival
+    // itself is counted after every store has completed.
     unsigned long long* ctr = p.tile_counters + (int64_t(m_tile) * p.tiles_n + n_tile);
     unsigned long long seen = 0;
     if (threadIdx.x == 0) seen = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -461,12 +466,18 @@ __device__ __forceinline__ void write_tile(const GemmParams& p, const v4f (&acc)
     if (threadIdx.x == 0) {
       unsigned long long old = seen;
       unsigned long long nxt;
-      do {
-        nxt = (unsigned(old >> 32) == p.epoch) ? old + 1 : ((unsigned long long)p.epoch << 32) | 1ull;
-      } while (!__hip_atomic_compare_exchange_strong(ctr, &old, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT));
+      for (;;) {
+        if (unsigned(old >> 32) == p.tag) {
+          nxt = __hip_atomic_fetch_add(ctr, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+          break;
+        }
+        nxt = ((unsigned long long)p.tag << 32) | 1ull;
+        if (__hip_atomic_compare_exchange_strong(ctr, &old, nxt, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT))
+          break;
+      }
       const bool last = unsigned(nxt) == unsigned(p.splits);
-      if (last) __hip_atomic_store(ctr, (unsigned long long)p.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (last) __hip_atomic_store(ctr, (unsigned long long)p.tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_arrival = last;
     }
     __syncthreads();

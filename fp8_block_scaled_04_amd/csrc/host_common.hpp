@@ -34,6 +34,20 @@ inline int effective_cus() {
   return (lim > 0 && lim < d) ? lim : d;
 }
 
+// Tag of the split-K arrival counters.  A call that runs to the end leaves
+// every counter word it used at (tag, 0), from which the next call with the
+// same tag counts with one atomic add per arrival; any other word is
+// restarted by its tile's first arrival.  The tag moves on only when a
+// launch fails, since a split call whose later launches never ran (a CU
+// limit cuts it into several) may leave counts part-way.  As FP32, and as
+// either BF16 half, the starting value is a signalling NaN, which no
+// partial sum or output of these kernels can hold.
+inline std::atomic<unsigned> g_counter_tag{0xFFA5C3E1u};
+inline unsigned counter_tag() { return g_counter_tag.load(); }
+inline void retire_counter_tag() {
+  if (g_counter_tag.fetch_add(1) + 1 == 0) g_counter_tag.fetch_add(1);
+}
+
 // Launches a GEMM of `units` work units (one workgroup each): all in one
 // launch, or, while a CU limit is in force, in consecutive launches of at
 // most that many workgroups, so that at most that many CUs run the GEMM at
@@ -47,7 +61,10 @@ inline int launch_units(Params& p, int64_t units, Launch&& launch_one) {
   const int64_t step = (lim > 0 && lim < device_cus() && units > lim) ? lim : units;
   for (int64_t off = 0; off < units; off += step) {
     p.unit_offset = int(off);
-    if (const int st = launch_one(std::min(step, units - off))) return st;
+    if (const int st = launch_one(std::min(step, units - off))) {
+      if (p.splits > 1) retire_counter_tag();
+      return st;
+    }
   }
   return 0;
 }
@@ -210,14 +227,6 @@ inline size_t counter_bytes(const DenseConfig& c) {
 
 inline size_t dense_workspace(const DenseConfig& c, int m, int n) {
   return c.splits > 1 ? counter_bytes(c) + size_t(c.splits) * size_t(m) * size_t(n) * sizeof(float) : 0;
-}
-
-// Per-call tag of the split-K arrival counters (never 0).
-inline std::atomic<unsigned> g_epoch{0};
-inline unsigned next_epoch() {
-  unsigned e = g_epoch.fetch_add(1) + 1;
-  if (e == 0) e = g_epoch.fetch_add(1) + 1;
-  return e;
 }
 
 }  // namespace host

@@ -633,7 +633,7 @@ int fp8_jit_gemm_nt(const uint8_t* lhs, int lhs_format, const float* lhs_scales,
   if (d.splits > 1) {
     p.tile_counters = static_cast<unsigned long long*>(workspace);
     p.partial = reinterpret_cast<float*>(static_cast<char*>(workspace) + counter_bytes(d));
-    p.epoch = next_epoch();
+    p.tag = counter_tag();
   }
   p.sa_ld = lhs_scales_ld;
   p.m = m; p.n = n; p.k = k; p.kg = k / 128; p.nb = int(cdiv(n, 128));

@@ -75,10 +75,14 @@ enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 };
  *              Pass at least fp8_gemm_workspace_bytes() bytes to allow
  *              split-K; a smaller (or NULL) workspace selects a configuration
  *              without split-K, which is never an error.  The workspace needs
- *              no initialisation (the counters are tagged per call) and is
- *              left in a state the next call accepts, also under HIP graph
- *              replay; two calls that may run concurrently must not share a
- *              workspace.  The last workgroup to finish a tile adds the
+ *              no initialisation (each counter carries a tag; a word without
+ *              the library's current tag is restarted) and is left in a
+ *              state the next call accepts, also under HIP graph replay;
+ *              two calls that may run concurrently must not share a
+ *              workspace.  A split call that fails with FP8G_ELAUNCH may
+ *              leave counts part-way: the library then moves to a new tag,
+ *              but a graph captured before the failure that uses the same
+ *              workspace must be captured again.  The last workgroup to finish a tile adds the
  *              partials in split order, so a given configuration always
  *              produces bit-identical output; results with and without
  *              split-K differ only by FP32 rounding order. */
@@ -98,8 +102,8 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
  * refused with FP8G_ESCRATCH before anything is launched (on a 256-CU
  * device the library's own configurations need at most about 16 MiB).
  * Every call on a device shares that device's array, which keeps the last
- * call's contents (nothing in it needs clearing: the arrival counters are
- * tagged per call): calls that may overlap on one device -- other streams,
+ * call's contents (nothing in it needs clearing: the arrival counters
+ * carry a tag, as with fp8_gemm_nt's workspace): calls that may overlap on one device -- other streams,
  * other threads, other graphs in flight -- race on it and must be
  * serialised (one stream) by the caller.  The first call on a device looks
  * up the array's device address (no allocation and no stream operation);

@@ -188,7 +188,7 @@ def _dense_dev(qa, sa, qb, sb):
 
 @pytest.mark.parametrize("m,n,k", [(8, 1024, 8192), (128, 512, 7168)])
 def test_splitk_workspace_needs_no_initialisation(m, n, k):
-    """The split-K arrival counters are tagged per call: a workspace full of
+    """The split-K arrival counters carry a tag: a workspace full of
     random bytes gives the same bits as a zeroed one, call after call."""
     require_gpu()
     qa, sa, qb, sb = dense_case(m, n, k, seed=11)
@@ -206,6 +206,38 @@ def test_splitk_workspace_needs_no_initialisation(m, n, k):
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
     assert_close(outs[0], oracle.gemm_nt(qa, sa, qb, sb), "split-K")
+
+
+def test_splitk_workspace_shared_by_shapes_in_turn():
+    """Split shapes with different tile grids and split counts take turns on
+    one workspace, so each one's counter words sit where another left
+    partial sums or counts: every call gives the bits of the same call on a
+    workspace of its own."""
+    require_gpu()
+    shapes = [(64, 2048, 7168), (128, 512, 7168), (8, 1024, 8192), (64, 4096, 7168)]
+    cases, refs = [], []
+    for i, (m, n, k) in enumerate(shapes):
+        desc = binding.fp8_gemm_describe(m, n, k)
+        say(f"dense {m}x{n}x{k}: {desc}")
+        assert "splits=1 " not in desc, desc
+        qa, sa, qb, sb = dense_case(m, n, k, seed=20 + i)
+        args = _dense_dev(qa, sa, qb, sb)
+        own = torch.zeros(binding.fp8_gemm_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device="cuda")
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        binding.fp8_gemm_nt(*args, out, workspace=own)
+        torch.cuda.synchronize()
+        cases.append((m, n, args))
+        refs.append(out.view(torch.int16).cpu().numpy())
+        if i == 0:
+            assert_close(refs[0].view(np.uint16), oracle.gemm_nt(qa, sa, qb, sb), "split-K, own workspace")
+    nbytes = max(binding.fp8_gemm_workspace_bytes(m, n, k) for m, n, k in shapes)
+    shared = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    for i in [0, 1, 2, 3, 3, 0, 2, 1, 0, 0, 3, 2]:
+        m, n, args = cases[i]
+        out = torch.empty((m, n), dtype=torch.bfloat16, device="cuda")
+        binding.fp8_gemm_nt(*args, out, workspace=shared)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.view(torch.int16).cpu().numpy(), refs[i]), f"shape {shapes[i]}"
 
 
 def test_splitk_graph_replay_matches_eager():
@@ -236,7 +268,7 @@ def test_splitk_graph_replay_matches_eager():
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(out.view(torch.int16).cpu().numpy(), ref), f"replay {rep}"
-        # eager work between replays (also moves the counters' epoch on)
+        # eager work on the same workspace between replays
         binding.fp8_gemm_nt(a, s_, b, t, eager, workspace=ws)
         torch.cuda.synchronize()
 

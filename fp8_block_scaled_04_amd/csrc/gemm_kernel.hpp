@@ -484,25 +484,43 @@ __device__ __forceinline__ void write_tile(const GemmParams& p, const v4f (&acc)
     if (!last_arrival) return;
     // Every split's partial of a 4-wide chunk (this one's too, read back
     // like the others) is requested before one wait, then added in split
-    // order.
+    // order.  With few splits a thread takes several chunks per wait (at
+    // most eight loads in flight), so a tile of more chunks than threads
+    // costs one or two memory round trips instead of one per chunk.  A
+    // chunk past the tile's edge reads the nearest chunk inside it and
+    // writes nothing.
     auto add_partials = [&](auto s_tag) {
       constexpr int S = decltype(s_tag)::value;
-      for (int c = threadIdx.x; c < CHUNKS; c += blockDim.x) {
-        const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
-        if (m0 + r < rows && n0 + c4 < shape_n) {
-          const float* P = p.partial + int64_t(m0 + r) * shape_n + n0 + c4;
-          const float* q[S];
+      constexpr int G = 8 / S;
+      for (int c0 = threadIdx.x; c0 < CHUNKS; c0 += G * blockDim.x) {
+        const float* q[G * S];
+        int64_t at[G];
+        bool live[G];
 #pragma unroll
-          for (int sp = 0; sp < S; ++sp) q[sp] = P + sp * mn;
-          v4f t[S];
-          load16_coherent<S>(q, t);
-          v4f sum = t[0];
+        for (int g = 0; g < G; ++g) {
+          const int c = c0 + g * blockDim.x;
+          const int r = c / (BN / 4), c4 = 4 * (c % (BN / 4));
+          live[g] = c < CHUNKS && m0 + r < rows && n0 + c4 < shape_n;
+          // clamped into the tile (a live chunk keeps its place); written
+          // without a select against the tile's base so that the tile
+          // indices stay in scalar registers for the whole kernel
+          const int rr = min(r, min(BM, rows - m0) - 1), cc = min(c4, min(BN, shape_n - n0) - 4);
+          at[g] = int64_t(m0 + rr) * shape_n + n0 + cc;
 #pragma unroll
-          for (int sp = 1; sp < S; ++sp) sum += t[sp];
+          for (int sp = 0; sp < S; ++sp) q[g * S + sp] = p.partial + at[g] + sp * mn;
+        }
+        v4f t[G * S];
+        load16_coherent<G * S>(q, t);
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          if (!live[g]) continue;
+          v4f sum = t[g * S];
+#pragma unroll
+          for (int sp = 1; sp < S; ++sp) sum += t[g * S + sp];
           uint2 v;
           v.x = pack_bf16x2(sum[0], sum[1]);
           v.y = pack_bf16x2(sum[2], sum[3]);
-          *reinterpret_cast<uint2*>(OUT + int64_t(m0 + r) * shape_n + n0 + c4) = v;
+          *reinterpret_cast<uint2*>(OUT + at[g]) = v;
         }
       }
     };

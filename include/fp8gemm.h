@@ -82,10 +82,11 @@ enum { FP8G_E4M3 = 0, FP8G_E5M2 = 1 };
  *              workspace.  A split call that fails with FP8G_ELAUNCH may
  *              leave counts part-way: the library then moves to a new tag,
  *              but a graph captured before the failure that uses the same
- *              workspace must be captured again.  The last workgroup to finish a tile adds the
- *              partials in split order, so a given configuration always
- *              produces bit-identical output; results with and without
- *              split-K differ only by FP32 rounding order. */
+ *              workspace must be captured again.  The last workgroup to
+ *              finish a tile adds the partials in split order, so a given
+ *              configuration always produces bit-identical output; results
+ *              with and without split-K differ only by FP32 rounding
+ *              order. */
 int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
                 const uint8_t* rhs, const float* rhs_scales,
                 uint16_t* out, int m, int n, int k,
@@ -103,9 +104,9 @@ int fp8_gemm_nt(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_
  * device the library's own configurations need at most about 16 MiB).
  * Every call on a device shares that device's array, which keeps the last
  * call's contents (nothing in it needs clearing: the arrival counters
- * carry a tag, as with fp8_gemm_nt's workspace): calls that may overlap on one device -- other streams,
- * other threads, other graphs in flight -- race on it and must be
- * serialised (one stream) by the caller.  The first call on a device looks
+ * carry a tag, as with fp8_gemm_nt's workspace): calls that may overlap on
+ * one device -- other streams, other threads, other graphs in flight --
+ * race on it and must be serialised (one stream) by the caller.  The first call on a device looks
  * up the array's device address (no allocation and no stream operation);
  * make one call before capturing the entry point in a HIP graph. */
 int fp8_gemm_nt_noalloc(const uint8_t* lhs, const float* lhs_scales, int64_t lhs_scales_ld,
@@ -253,7 +254,9 @@ int fp8_jit_config_supported(int mode, const fp8_gemm_config* config);
  * launching it: the warm-up before timing.  Without a device it only fills
  * the disk cache. */
 int fp8_jit_warmup(int mode, int n, int k, int lhs_format, int rhs_format, const fp8_gemm_config* config);
-/* Split-K workspace of fp8_jit_gemm_nt for this configuration (0 if none). */
+/* Split-K workspace of fp8_jit_gemm_nt for this configuration (0 if none);
+ * fp8_jit_gemm_nt uses it as fp8_gemm_nt uses its workspace (same layout,
+ * same counter tag, no initialisation needed). */
 size_t fp8_jit_gemm_workspace_bytes(int m, int n, int k, const fp8_gemm_config* config);
 int fp8_jit_gemm_nt(const uint8_t* lhs, int lhs_format, const float* lhs_scales, int64_t lhs_scales_ld,
                     const uint8_t* rhs, int rhs_format, const float* rhs_scales,

@@ -79,6 +79,34 @@ def test_tile_configs_match_the_oracle(ci, specialize):
         assert_close(again, oracle.gemm_nt(qa, sa, qb, sb), "no workspace")
 
 
+# (split count, k): 13, 14 or 24 K groups, so that each count is one the
+# equal runs of K groups actually give
+SPLIT_CASES = [(2, 1664), (3, 1664), (4, 1664), (5, 1664), (6, 3072), (7, 1792), (8, 3072)]
+SPLIT_TILES = [
+    dict(block_m=64, block_n=32, waves_m=4, waves_n=1, waves_k=1, stages=4, k_per_stage=1),    # 2 chunks per thread
+    dict(block_m=128, block_n=128, waves_m=4, waves_n=2, waves_k=1, stages=3, k_per_stage=1),  # 8 chunks per thread
+]
+
+
+@pytest.mark.parametrize("ti", range(len(SPLIT_TILES)))
+@pytest.mark.parametrize("splits,k", SPLIT_CASES)
+def test_every_split_count_matches_the_oracle(splits, k, ti):
+    """The last arrival adds 2..8 partials, several chunks per wait when the
+    splits are few; tails in M and N leave chunks past the tile's edge."""
+    require_gpu()
+    m, n = 200, 1032
+    config = dict(SPLIT_TILES[ti], splits=splits, specialize=0)
+    assert binding.fp8_jit_config_supported(D, config), config
+    tiles = -(-m // config["block_m"]) * -(-n // config["block_n"])
+    counters = -(-tiles * 8 // 256) * 256
+    assert (binding.fp8_jit_gemm_workspace_bytes(m, n, k, config) - counters) // (m * n * 4) == splits
+    say(f"jit split-K tile {ti} splits={splits} k={k}")
+    qa, sa, qb, sb = dense_case(m, n, k, seed=40 + splits)
+    got = run_jit(qa, sa, qb, sb, config=config)
+    assert_close(got, oracle.gemm_nt(qa, sa, qb, sb), f"splits={splits} tile {ti}")
+    assert np.array_equal(run_jit(qa, sa, qb, sb, config=config), got)
+
+
 def test_e5m2_specialised():
     require_gpu()
     m, n, k = 96, 4096, 2048
